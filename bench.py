@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark: busBW of the N-rank ring all-reduce on one MI355X.
+
+One step is one ring all-reduce (reduce-scatter stages then all-gather stages,
+every channel and chunk) of the headline workload: 8 simulated ranks, 64 MiB
+of fp32 per rank drawn N(0,1), 8 channels, 512 KiB chunks, sum. The inputs are
+resident in HBM before the timed region starts. Prints ONE JSON line on
+stdout; details go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--no-check]
+
+busBW = algBW * 2(N-1)/N with algBW = bytes per rank / time per step
+(the ring cost model's nSteps/nRanks factor, "NCCL" book, ch. 5, ring.cc).
+The roofline entry divides the algorithmic HBM bytes of one launch,
+(6N-4) * S for the all-reduce, by the average launch duration measured with
+HIP events on the launch stream, against the 8 TB/s HBM3E peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "busBW GB/s of N-rank ring all-reduce on 1 MI355X; % of HBM peak"
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "ring_all_reduce_allreduce_amd", "csrc", f)
+    for f in ("ringsim_kernels.hip", "ring_plan.h", "ringsim_internal.h")
+]
+
+# Named single-GPU workloads. "ar8x64" is the headline; the others exist for
+# exploration and print the same JSON fields.
+WORKLOADS = {
+    "ar8x64": dict(coll="allreduce", nranks=8, count=16_777_216, dtype="float32", nchannels=8,
+                   chunk_bytes=524_288, synth_workload=2, op="sum",
+                   desc="ring all-reduce sum, 8 simulated ranks x 64 MiB fp32 (16,777,216 elems, N(0,1)), "
+                        "8 channels, 512 KiB chunks"),
+    "ar8x25bf16": dict(coll="allreduce", nranks=8, count=13_107_200, dtype="bfloat16", nchannels=16,
+                       chunk_bytes=524_288, synth_workload=3, op="sum",
+                       desc="DDP bucket ring all-reduce sum, 8 simulated ranks x 25 MiB bf16 "
+                            "(13,107,200 elems, N(0,1e-3)), 16 channels"),
+    "ar16x256i32": dict(coll="allreduce", nranks=16, count=67_108_864, dtype="int32", nchannels=16,
+                        chunk_bytes=524_288, synth_workload=4, op="sum",
+                        desc="ring all-reduce sum, 16 simulated ranks x 256 MiB int32, 16 channels"),
+    "rs8x128bf16": dict(coll="reduce_scatter", nranks=8, count=67_108_864, dtype="bfloat16", nchannels=8,
+                        chunk_bytes=524_288, synth_workload=5, op="sum",
+                        desc="ring reduce-scatter sum, 8 simulated ranks x 128 MiB bf16 in, 16 MiB out"),
+    "ag8x128bf16": dict(coll="all_gather", nranks=8, count=67_108_864, dtype="bfloat16", nchannels=8,
+                        chunk_bytes=524_288, synth_workload=5, op="sum",
+                        desc="ring all-gather, 8 simulated ranks x 16 MiB bf16 in, 128 MiB out"),
+    "a2a8x32bf16": dict(coll="alltoall", nranks=8, count=16_777_216, dtype="bfloat16", nchannels=1,
+                        chunk_bytes=524_288, synth_workload=5, op="sum",
+                        desc="all-to-all, 8 simulated ranks x 8 chunks of 512x4096 bf16 (32 MiB per rank)"),
+}
+DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32", "int64": "i64"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(coll: str, n: int, s: int) -> int:
+    """HBM bytes the ring method moves in one launch, summed over ranks; S is
+    the full per-rank buffer (all-reduce buffer, reduce-scatter input,
+    all-gather output, all-to-all buffer). All-reduce: every rank reads S,
+    writes S and writes then reads 2(N-1)/N * S of FIFO slots; reduce-scatter
+    and all-gather: (3N-1)/N * S per rank; all-to-all: 2S per rank."""
+    if n == 1:
+        return 2 * s
+    if coll == "allreduce":
+        return (6 * n - 4) * s
+    if coll in ("reduce_scatter", "all_gather"):
+        return (3 * n - 1) * s
+    return 2 * n * s
+
+
+def bus_factor(coll: str, n: int) -> float:
+    if n == 1:
+        return 1.0
+    return 2.0 * (n - 1) / n if coll == "allreduce" else (n - 1) / n
+
+
+def load_traffic(name: str, src_hash: str):
+    """Counter-measured HBM bytes per launch, if a summary for this workload
+    and this exact kernel source is committed under profiles/."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def make_inputs(w: dict):
+    import numpy as np
+    import synth
+
+    n, dtype = w["nranks"], w["dtype"]
+    if w["coll"] == "alltoall":
+        return synth.a2a_inputs(nranks=n)
+    if w["coll"] == "all_gather":
+        return synth.rank_inputs(w["synth_workload"], n, w["count"] // n, dtype, "normal", 1.0, bucket=2)
+    if w["coll"] == "reduce_scatter":
+        return synth.rank_inputs(w["synth_workload"], n, w["count"], dtype, "normal", 1.0)
+    if w["synth_workload"] == 4:
+        return synth.rank_inputs(4, n, w["count"], dtype, "int", lo=-(1 << 20), hi=(1 << 20))
+    xs = synth.workload_inputs(w["synth_workload"])
+    assert xs[0].shape[0] == w["count"] and len(xs) == n
+    _ = np
+    return xs
+
+
+def oracle_call(w: dict, xs):
+    import oracle
+
+    if w["coll"] == "allreduce":
+        return oracle.ring_allreduce(xs, w["op"], w["dtype"], nchannels=w["nchannels"], chunk_bytes=w["chunk_bytes"])
+    if w["coll"] == "reduce_scatter":
+        return oracle.ring_reduce_scatter(xs, w["op"], w["dtype"], nchannels=w["nchannels"],
+                                          chunk_bytes=w["chunk_bytes"])
+    if w["coll"] == "all_gather":
+        return oracle.ring_all_gather(xs, w["dtype"], nchannels=w["nchannels"], chunk_bytes=w["chunk_bytes"])
+    return oracle.alltoall(xs, w["dtype"])
+
+
+def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 20.0) -> dict:
+    """The oracle, as it stands, timed on this host on the same workload."""
+    import numpy as np  # noqa: F401
+
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while not times or (time.perf_counter() < t_end and len(times) < 7):
+        t0 = time.perf_counter()
+        oracle_call(w, xs)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    n = w["nranks"]
+    busbw = per_rank_bytes / t * bus_factor(w["coll"], n) / 1e9
+    return {
+        "value": round(busbw, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the full workload ({w['desc']}), NumPy ring replay, median of {len(times)} runs, "
+                  f"{t:.3f} s per call; host has {len(os.sched_getaffinity(0))} cores available",
+    }
+
+
+def d2d_copy_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """1 GiB device-to-device copy (read + write bytes / time) as the
+    achievable-bandwidth context of this box."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return 2 * nbytes / t / 1e9
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ar8x64", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--wpc", type=int, default=0, help="workgroups per channel (0 = library default)")
+    ap.add_argument("--slot-bytes", type=int, default=0)
+    ap.add_argument("--nslots", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build simulates all ranks on ONE GPU; run it with --gpus 1 "
+              "(multi-GPU rings over xGMI are not part of it)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ring_all_reduce_allreduce_amd as rs
+
+    w = WORKLOADS[args.workload]
+    n, dtype, coll = w["nranks"], w["dtype"], w["coll"]
+    esize = rs.ELEM_SIZE[dtype]
+    tdt = {"float32": torch.float32, "bfloat16": torch.bfloat16, "int32": torch.int32, "int64": torch.int64}[dtype]
+    dev = torch.device("cuda:0")
+
+    log(f"[bench] workload {args.workload}: {w['desc']}")
+    xs = make_inputs(w)
+
+    def upload(x):
+        if dtype == "bfloat16":
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    send = [upload(x) for x in xs]
+    if coll == "allreduce":
+        recv = [torch.empty_like(s) for s in send]
+        per_rank_bytes = w["count"] * esize
+        call = lambda: rs.allreduce(comm, send, recv, op=w["op"])  # noqa: E731
+    elif coll == "reduce_scatter":
+        recv = [torch.empty(w["count"] // n, dtype=tdt, device=dev) for _ in range(n)]
+        per_rank_bytes = w["count"] * esize
+        call = lambda: rs.reduce_scatter(comm, send, recv, op=w["op"])  # noqa: E731
+    elif coll == "all_gather":
+        recv = [torch.empty(w["count"], dtype=tdt, device=dev) for _ in range(n)]
+        per_rank_bytes = w["count"] * esize
+        call = lambda: rs.all_gather(comm, send, recv)  # noqa: E731
+    else:
+        recv = [torch.empty_like(s) for s in send]
+        per_rank_bytes = xs[0].shape[0] * esize
+        call = lambda: rs.alltoall(comm, send, recv)  # noqa: E731
+
+    comm = rs.comm_init(n, w["nchannels"], "auto", chunk_bytes=w["chunk_bytes"],
+                        workgroups_per_channel=args.wpc or None, slot_bytes=args.slot_bytes or None,
+                        nslots=args.nslots or None)
+    info = rs.comm_query(comm)
+    log(f"[bench] comm {json.dumps(info)}")
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    if rs.get_async_error(comm) != rs.SUCCESS:
+        log("[bench] warmup left the communicator in error state")
+        return 1
+
+    # Correctness of the timed configuration against the oracle.
+    check = None
+    if not args.no_check:
+        want = oracle_call(w, xs)
+        ok = True
+        for r in range(n):
+            got = recv[r].view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" else recv[r].cpu().numpy()
+            ok &= bool(np.array_equal(got.view(np.uint8), np.asarray(want[r]).view(np.uint8)))
+        check = "bit-exact vs oracle" if ok else "MISMATCH vs oracle"
+        log(f"[bench] parity: {check}")
+        if not ok:
+            return 1
+
+    # Timed region: K steps, per-launch HIP events on the launch stream.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        call()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if rs.get_async_error(comm) != rs.SUCCESS:
+        log("[bench] timed region left the communicator in error state")
+        return 1
+    per = [s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends)]
+    t_med = statistics.median(per)
+    t_avg = sum(per) / len(per)
+    t_p95 = sorted(per)[min(len(per) - 1, int(0.95 * len(per)))]
+    cv = statistics.pstdev(per) / t_avg if len(per) > 1 else 0.0
+    ms_per_step = wall / args.steps * 1e3
+
+    algbw = per_rank_bytes / t_med / 1e9
+    busbw = algbw * bus_factor(coll, n)
+    bytes_alg = algorithmic_bytes(coll, n, per_rank_bytes)
+    achieved = bytes_alg / t_avg / 1e9
+    compulsory = 2 * n * per_rank_bytes if coll in ("allreduce", "alltoall") else (n + 1) * per_rank_bytes
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(args.workload, src_hash)
+    d2d = d2d_copy_gbs()
+    log(f"[bench] per-launch median {t_med * 1e6:.1f} us, avg {t_avg * 1e6:.1f} us, p95 {t_p95 * 1e6:.1f} us, "
+        f"CV {cv * 100:.2f}%  algBW {algbw:.1f} GB/s busBW {busbw:.1f} GB/s  "
+        f"alg-bytes rate {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)  "
+        f"compulsory rate {compulsory / t_avg / 1e9:.0f} GB/s  D2D copy {d2d:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(w, xs, per_rank_bytes)
+        log(f"[bench] cpu baseline {cpu}")
+
+    kernel_name = {"allreduce": "ring_bulk_kernel (all-reduce)", "reduce_scatter": "ring_bulk_kernel (reduce-scatter)",
+                   "all_gather": "ring_bulk_kernel (all-gather)", "alltoall": "copy_kernel (all-to-all)"}[coll]
+    out = {
+        "metric": METRIC,
+        "value": round(busbw, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_TAG[dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": w["desc"],
+            "collective": coll,
+            "simulated_ranks": n,
+            "bytes_per_rank": per_rank_bytes,
+            "nchannels": w["nchannels"],
+            "chunk_bytes": w["chunk_bytes"],
+            "workgroups_per_channel": info["workgroups_per_channel"],
+            "proto": "bulk",
+            "parallelism": "1 GPU, simulated ranks",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_name,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": bytes_alg,
+            "launch_avg_us": round(t_avg * 1e6, 2),
+        },
+        "cpu_baseline": cpu,
+        "extra": {
+            "algbw_gbs": round(algbw, 2),
+            "busbw_gbs": round(busbw, 2),
+            "t_median_us": round(t_med * 1e6, 2),
+            "t_p95_us": round(t_p95 * 1e6, 2),
+            "cv": round(cv, 4),
+            "frac_compulsory": round(compulsory / t_avg / 1e9 / HBM_PEAK_GBS, 4),
+            "d2d_copy_gbs": round(d2d, 1),
+            "parity": check,
+            "kernel_source_hash": src_hash,
+        },
+    }
+    rs.comm_destroy(comm)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,217 @@
+/*
+ * ringsim.h -- C ABI of libringsim: ring collectives over N simulated ranks
+ * that live in the HBM of one MI355X (gfx950).
+ *
+ * Every simulated rank r owns a send buffer and a receive buffer in device
+ * memory. Ranks exchange data only through FIFO staging slots that the
+ * library keeps in HBM, one FIFO per (sender -> receiver, channel, workgroup
+ * lane), guarded by step counters. The collectives follow the ring schedule
+ * of NCCL as described in the "NCCL" book (aireadcode.com), ch. 2: s. 2.2
+ * (channels split the data), s. 2.3 (RingARAlgorithm: loops, chunks and the
+ * chunk visited at every stage), s. 2.4 (Simple and LL protocols, FIFO
+ * head/tail counters). Semantics of the collectives follow the collectives
+ * table of "AI Systems Performance Engineering (3)".
+ *
+ * Conventions shared by every call:
+ *   - Pointers named *bufs are HOST arrays of length nranks holding DEVICE
+ *     pointers (one per simulated rank). The caller owns all of them; the
+ *     library never frees or retains them beyond the enqueued work.
+ *   - Buffers of one call must not overlap across ranks, except that a rank's
+ *     send and receive buffers may alias exactly as described per call.
+ *   - Device buffers should be 16-byte aligned; buffers aligned only to their
+ *     element size take a slower element-wise path. Misaligned elements are
+ *     rejected with RINGSIM_INVALID_ARGUMENT.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream): they return once the work is enqueued, like ncclAllReduce as
+ *     called from PyTorch's ProcessGroupNCCL ("NCCL 专家课程 29:
+ *     ProcessGroupNCCL、Stream、Event 与 Work"). Calls on one communicator must
+ *     be issued from one host thread and must be ordered on the device (one
+ *     stream, or streams ordered by events): the FIFOs are shared state.
+ *   - count == 0 is a successful no-op; nranks == 1 is a local copy
+ *     ("NCCL" book, enqueue chapter, taskAppend).
+ *   - Every kernel polls an abort word and bounds each wait by a timeout; a
+ *     call whose kernel gave up leaves the communicator in error state, which
+ *     ringsim_get_async_error reports and every later call returns.
+ */
+#ifndef RINGSIM_H
+#define RINGSIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RINGSIM_VERSION_MAJOR 0
+#define RINGSIM_VERSION_MINOR 1
+#define RINGSIM_MAX_RANKS 64
+#define RINGSIM_MAX_CHANNELS 64
+#define RINGSIM_MAX_WORKGROUPS_PER_CHANNEL 16
+
+/* Opaque communicator. Allocated by ringsim_comm_init*, released by
+ * ringsim_comm_destroy. Guarded by magic words at both ends ("NCCL" book,
+ * s. 2.1, startMagic/endMagic) and a registry of live handles: a destroyed or
+ * foreign handle yields RINGSIM_INVALID_USAGE. */
+typedef struct ringsim_comm* ringsim_comm_t;
+
+/* A hipStream_t passed as an untyped pointer so that this header needs no
+ * HIP headers. */
+typedef void* ringsim_stream_t;
+
+/* Result codes. The numbering follows NCCL's public result names; "invalid
+ * usage = 5" is the one value the pages print ("NCCL 专家课程 17", failure
+ * experiments), the others are this library's reading. */
+typedef enum {
+  RINGSIM_SUCCESS = 0,
+  RINGSIM_UNHANDLED_DEVICE_ERROR = 1, /* a HIP call failed */
+  RINGSIM_SYSTEM_ERROR = 2,           /* host allocation failed */
+  RINGSIM_INTERNAL_ERROR = 3,         /* a kernel timed out waiting on a peer */
+  RINGSIM_INVALID_ARGUMENT = 4,       /* bad pointer, size, dtype, op, rank count */
+  RINGSIM_INVALID_USAGE = 5,          /* bad / destroyed handle, impossible config */
+  RINGSIM_IN_PROGRESS = 7,            /* queried work has not finished yet */
+  RINGSIM_ABORTED = 8                 /* ringsim_abort was called */
+} ringsim_result_t;
+
+typedef enum {
+  RINGSIM_INT32 = 0,
+  RINGSIM_INT64 = 1,
+  RINGSIM_FLOAT32 = 2,
+  RINGSIM_BFLOAT16 = 3
+} ringsim_datatype_t;
+
+/* Reduction operators. Floating-point hops are rounded to the buffer type
+ * (round-to-nearest-even, subnormals kept); bf16 hops compute in fp32 and
+ * round once to bf16. max/min order -0 below +0. Integers wrap. */
+typedef enum {
+  RINGSIM_SUM = 0,
+  RINGSIM_PROD = 1,
+  RINGSIM_MAX = 2,
+  RINGSIM_MIN = 3
+} ringsim_redop_t;
+
+/* Protocols ("NCCL" book, s. 2.4): BULK keeps readiness in separate step
+ * counters (Simple); FLAG packs a 4-byte flag with every 4 bytes of payload
+ * so the receiver polls the data itself (LL). AUTO picks FLAG below
+ * flag_threshold_bytes per rank, BULK otherwise. */
+typedef enum {
+  RINGSIM_PROTO_AUTO = 0,
+  RINGSIM_PROTO_BULK = 1,
+  RINGSIM_PROTO_FLAG = 2
+} ringsim_proto_t;
+
+typedef enum {
+  RINGSIM_COLL_ALLREDUCE = 0,
+  RINGSIM_COLL_REDUCE_SCATTER = 1,
+  RINGSIM_COLL_ALL_GATHER = 2,
+  RINGSIM_COLL_ALLTOALL = 3
+} ringsim_coll_t;
+
+/* Tunables; zero fields take the default. */
+typedef struct {
+  size_t chunk_bytes;          /* ring chunk per channel; default 524288; multiple of 16 */
+  int workgroups_per_channel;  /* workgroups per (rank, channel); default chosen from the CU count */
+  size_t slot_bytes;           /* bulk FIFO slot; default 32768; multiple of 4096 */
+  int nslots;                  /* bulk FIFO depth; default 8 (NCCL_STEPS) */
+  int timeout_ms;              /* bound on any single wait; default 10000, env RINGSIM_TIMEOUT_MS */
+  size_t flag_threshold_bytes; /* AUTO: FLAG below this many bytes per rank; default 65536 */
+} ringsim_config_t;
+
+/* Read-only description of a communicator. */
+typedef struct {
+  int nranks;
+  int nchannels;
+  int proto;
+  int workgroups_per_channel;
+  int nslots;
+  int device;
+  size_t chunk_bytes;
+  size_t slot_bytes;
+  size_t flag_threshold_bytes;
+  size_t fifo_bytes;           /* bulk FIFO bytes in HBM */
+  size_t flag_fifo_bytes;      /* flag-packed FIFO bytes in HBM */
+  int max_resident_workgroups; /* co-resident workgroups the device can hold */
+  int compute_units;
+  uint64_t calls;              /* collective calls enqueued so far */
+} ringsim_comm_info_t;
+
+/* Fills *cfg with the defaults (environment overrides included). */
+ringsim_result_t ringsim_config_default(ringsim_config_t* cfg);
+
+/* Creates a communicator of `nranks` (1..RINGSIM_MAX_RANKS) simulated ranks
+ * on the current HIP device, with `nchannels` (1..RINGSIM_MAX_CHANNELS) ring
+ * channels and protocol `proto` (ringsim_proto_t). Ring order is
+ * r -> (r + 1) mod nranks. Allocates the FIFOs and counters in HBM once;
+ * synchronous. On error *comm is left untouched: bad arguments give
+ * RINGSIM_INVALID_ARGUMENT, a configuration whose workgroups cannot all be
+ * resident at once gives RINGSIM_INVALID_USAGE, a failed HIP allocation
+ * RINGSIM_UNHANDLED_DEVICE_ERROR. */
+ringsim_result_t ringsim_comm_init(ringsim_comm_t* comm, int nranks, int nchannels, int proto);
+
+/* As ringsim_comm_init with explicit tunables (cfg may be NULL). */
+ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int nchannels, int proto,
+                                          const ringsim_config_t* cfg);
+
+/* Waits for the communicator's last stream, frees its device memory and
+ * invalidates the handle. */
+ringsim_result_t ringsim_comm_destroy(ringsim_comm_t comm);
+
+ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* info);
+
+/* Ring all-reduce ("AI Systems Performance Engineering (3)", collectives
+ * table: every rank receives the reduction; equal to reduce-scatter followed
+ * by all-gather). count elements per rank; recvbufs[r] may equal
+ * sendbufs[r] (in place). Chunk k of every loop is folded in rank order
+ * k+1, k+2, ..., k ("NCCL" book, s. 2.3, chunk id per stage). */
+ringsim_result_t ringsim_allreduce(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                   size_t count, int dtype, int op, ringsim_stream_t stream);
+
+/* Ring reduce-scatter (same table: each rank keeps one block of the
+ * reduction). sendbufs[r] holds nranks * recvcount elements; recvbufs[r]
+ * receives the reduced block r, folded in rank order r+1, ..., r. recvbufs[r]
+ * may equal sendbufs[r] + r * recvcount elements (in place). */
+ringsim_result_t ringsim_reduce_scatter(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                        size_t recvcount, int dtype, int op, ringsim_stream_t stream);
+
+/* Ring all-gather (same table; slice order of "NCCL 专家课程 17", section
+ * "Bootstrap Ring 与 AllGather"). sendbufs[r] holds sendcount elements;
+ * block b of recvbufs[r] (nranks * sendcount elements) receives sendbufs[b].
+ * sendbufs[r] may equal recvbufs[r] + r * sendcount elements (in place). */
+ringsim_result_t ringsim_all_gather(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                    size_t sendcount, int dtype, ringsim_stream_t stream);
+
+/* All-to-all (same table: chunk j of rank i goes to rank j). Both buffers of
+ * a rank hold nranks * count elements; block i of recvbufs[j] receives block
+ * j of sendbufs[i]. Send and receive buffers must not overlap. */
+ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                  size_t count, int dtype, ringsim_stream_t stream);
+
+/* Reports the communicator's asynchronous state: RINGSIM_SUCCESS,
+ * RINGSIM_IN_PROGRESS while enqueued work is still running and no error is
+ * known, or the error a kernel or ringsim_abort left behind. */
+ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error);
+
+/* Raises the abort word that every spinning kernel polls; running kernels
+ * stop waiting and finish, and every later call returns RINGSIM_ABORTED. */
+ringsim_result_t ringsim_abort(ringsim_comm_t comm);
+
+/* Static text for a result code. */
+const char* ringsim_get_error_string(ringsim_result_t result);
+
+/* Host-only view of the partition used by the kernels. For `coll`
+ * (ringsim_coll_t), writes rows of 5 int64 values
+ *   (channel, loop, chunk, begin, end)
+ * with [begin, end) absolute element indices: for the all-reduce, chunk k of
+ * every loop of every channel of a count-element buffer; for reduce-scatter
+ * and all-gather (chunk = -1), the element range of every loop of every
+ * channel inside one rank block of `count` elements. Writes at most max_rows
+ * rows to `rows` (host memory, may be NULL to query) and the total number to
+ * *nrows. Touches no device. */
+ringsim_result_t ringsim_debug_plan(int coll, size_t count, int nranks, int nchannels, size_t chunk_bytes,
+                                    int dtype, int64_t* rows, size_t max_rows, size_t* nrows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGSIM_H */

@@ -1,0 +1,560 @@
+// ringsim_api.hip -- host side of libringsim: communicator, validation,
+// protocol choice, plan parameters and kernel launch. Exports the C ABI of
+// include/ringsim.h.
+//
+// Call path ("NCCL" book, enqueue chapter: ncclEnqueueCheck -> taskAppend ->
+// plan -> launch, collapsed): check the handle and its magic words, check the
+// arguments, return early for count == 0, copy locally for one rank, choose
+// the protocol by size, fill one kernel-argument block and enqueue one kernel
+// on the caller's stream. Nothing waits for the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "ring_plan.h"
+#include "ringsim_internal.h"
+
+using namespace ringsim;
+
+namespace {
+
+// Sentinels at both ends of the communicator ("NCCL" book, s. 2.1: first and
+// last field of ncclComm, checked to catch use after destroy).
+constexpr uint64_t kLiveMagic = 0x52494e4753494d31ull;  // "RINGSIM1"
+constexpr uint64_t kDeadMagic = 0xdeaddeaddeaddeadull;
+
+enum LogLevel { kLogNone = 0, kLogWarn = 1, kLogInfo = 2 };
+
+int log_level() {
+  static const int level = [] {
+    const char* e = std::getenv("RINGSIM_DEBUG");
+    if (!e) return (int)kLogNone;
+    if (!std::strcmp(e, "INFO")) return (int)kLogInfo;
+    if (!std::strcmp(e, "WARN")) return (int)kLogWarn;
+    return (int)kLogNone;
+  }();
+  return level;
+}
+
+#define RS_LOG(lvl, ...)                                   \
+  do {                                                     \
+    if (log_level() >= (lvl)) {                            \
+      std::fprintf(stderr, "ringsim %s: ", (lvl) == kLogWarn ? "WARN" : "INFO"); \
+      std::fprintf(stderr, __VA_ARGS__);                   \
+      std::fprintf(stderr, "\n");                          \
+    }                                                      \
+  } while (0)
+
+long env_long(const char* name, long dflt) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return dflt;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  return (end && *end == 0) ? v : dflt;
+}
+
+}  // namespace
+
+struct ringsim_comm {
+  uint64_t start_magic;
+  int nranks;
+  int nchannels;
+  int proto;
+  int wpc;
+  int nslots;
+  int device;
+  size_t chunk_bytes;
+  size_t slot_bytes;
+  size_t flag_threshold;
+  int timeout_ms;
+  uint64_t timeout_ticks;
+  int compute_units;
+  int blocks_per_cu;
+  char* fifo;
+  size_t fifo_bytes;
+  char* flag_fifo;
+  size_t flag_fifo_bytes;
+  FifoCtr* ctr;
+  size_t ctr_bytes;
+  uint32_t* dev_abort;
+  uint32_t* host_words;      // [0] abort request, [1] kernel error (host view)
+  uint32_t* host_words_dev;  // the same words as the device sees them
+  uint64_t calls;
+  ringsim_result_t sticky;
+  hipStream_t last_stream;
+  bool has_last_stream;
+  uint64_t end_magic;
+};
+
+namespace {
+
+std::mutex g_live_mu;
+std::unordered_set<const ringsim_comm*> g_live;
+
+bool is_live(const ringsim_comm* c) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return g_live.count(c) != 0;
+}
+
+ringsim_result_t check_comm(const ringsim_comm* c) {
+  if (!c || !is_live(c)) return RINGSIM_INVALID_USAGE;
+  if (c->start_magic != kLiveMagic || c->end_magic != kLiveMagic) return RINGSIM_INVALID_USAGE;
+  return RINGSIM_SUCCESS;
+}
+
+// Folds the device-visible error words into the sticky result.
+ringsim_result_t poll_async(ringsim_comm* c) {
+  if (c->sticky != RINGSIM_SUCCESS) return c->sticky;
+  const uint32_t abort_req = __atomic_load_n(&c->host_words[0], __ATOMIC_ACQUIRE);
+  const uint32_t kerr = __atomic_load_n(&c->host_words[1], __ATOMIC_ACQUIRE);
+  if (abort_req || kerr == kErrAborted) {
+    c->sticky = RINGSIM_ABORTED;
+  } else if (kerr == kErrTimeout) {
+    c->sticky = RINGSIM_INTERNAL_ERROR;
+    RS_LOG(kLogWarn, "a ring kernel gave up waiting for a peer (timeout %d ms)", c->timeout_ms);
+  }
+  return c->sticky;
+}
+
+bool valid_dtype(int dtype) { return dtype >= RINGSIM_INT32 && dtype <= RINGSIM_BFLOAT16; }
+bool valid_op(int op) { return op >= RINGSIM_SUM && op <= RINGSIM_MIN; }
+
+// Device buffers: non-null, element aligned; `vec` reports 16-byte alignment.
+ringsim_result_t check_bufs(const ringsim_comm* c, const void* const* sb, void* const* rb, int esize,
+                            bool* vec) {
+  if (!sb || !rb) return RINGSIM_INVALID_ARGUMENT;
+  bool v = true;
+  for (int r = 0; r < c->nranks; ++r) {
+    const uintptr_t s = (uintptr_t)sb[r];
+    const uintptr_t d = (uintptr_t)rb[r];
+    if (!s || !d) return RINGSIM_INVALID_ARGUMENT;
+    if ((s % esize) || (d % esize)) return RINGSIM_INVALID_ARGUMENT;
+    if ((s & 15u) || (d & 15u)) v = false;
+  }
+  *vec = v;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t check_device(const ringsim_comm* c) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  return dev == c->device ? RINGSIM_SUCCESS : RINGSIM_INVALID_USAGE;
+}
+
+void fill_common(const ringsim_comm* c, RingArgs* a, const void* const* sb, void* const* rb) {
+  std::memset(a, 0, sizeof(*a));
+  for (int r = 0; r < c->nranks; ++r) {
+    a->send[r] = static_cast<const char*>(sb[r]);
+    a->recv[r] = static_cast<char*>(rb[r]);
+  }
+  a->nranks = c->nranks;
+  a->nchannels = c->nchannels;
+  a->ctr = c->ctr;
+  a->pipe_stride = c->nchannels * c->wpc;
+  a->pipe_mul = c->wpc;
+  a->dev_abort = c->dev_abort;
+  a->host_abort = c->host_words_dev;
+  a->host_err = c->host_words_dev + 1;
+  a->timeout_ticks = c->timeout_ticks;
+}
+
+// Picks the protocol and fills the protocol-dependent launch geometry.
+void fill_proto(const ringsim_comm* c, RingArgs* a, size_t bytes_per_rank, int esize, bool* flag) {
+  bool f = c->proto == RINGSIM_PROTO_FLAG ||
+           (c->proto == RINGSIM_PROTO_AUTO && bytes_per_rank < c->flag_threshold);
+  *flag = f;
+  if (f) {
+    a->wpc = 1;
+    a->fifo = c->flag_fifo;
+    a->fifo_stride = c->nchannels;
+    a->fifo_mul = 1;
+    a->nslots = kFlagSlots;
+    a->slot_bytes = kFlagSlotBytes;
+    a->chunk = (int64_t)std::min<size_t>(c->chunk_bytes, (size_t)kFlagChunkBytes) / esize;
+  } else {
+    a->wpc = c->wpc;
+    a->fifo = c->fifo;
+    a->fifo_stride = c->nchannels * c->wpc;
+    a->fifo_mul = c->wpc;
+    a->nslots = c->nslots;
+    a->slot_bytes = (int)c->slot_bytes;
+    a->chunk = (int64_t)c->chunk_bytes / esize;
+  }
+}
+
+ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void* const* rb, size_t bytes,
+                                   hipStream_t s) {
+  if (sb[0] == rb[0] || bytes == 0) return RINGSIM_SUCCESS;
+  CopyArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  ca.src[0] = static_cast<const char*>(sb[0]);
+  ca.dst[0] = static_cast<char*>(rb[0]);
+  ca.block_bytes = (int64_t)bytes;
+  ca.nranks = 1;
+  ca.transpose = 0;
+  ca.vec_ok = ((((uintptr_t)sb[0]) | ((uintptr_t)rb[0])) & 15u) == 0;
+  if (launch_copy(ca, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
+                          int dtype, int op, ringsim_stream_t stream) {
+  ringsim_result_t res = check_comm(c);
+  if (res != RINGSIM_SUCCESS) return res;
+  if ((res = poll_async(c)) != RINGSIM_SUCCESS) return res;
+  if (!valid_dtype(dtype) || !valid_op(op)) return RINGSIM_INVALID_ARGUMENT;
+  const int esize = dtype_size(dtype);
+  const int64_t n = c->nranks;
+  if (count > (size_t)(INT64_MAX / 16) / (size_t)n / (size_t)esize) return RINGSIM_INVALID_ARGUMENT;
+  if (count == 0) return RINGSIM_SUCCESS;
+  bool vec = false;
+  if ((res = check_bufs(c, sb, rb, esize, &vec)) != RINGSIM_SUCCESS) return res;
+  if ((res = check_device(c)) != RINGSIM_SUCCESS) return res;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  c->calls++;
+  c->last_stream = s;
+  c->has_last_stream = true;
+  if (n == 1) {
+    // A single rank is a local copy ("NCCL" book, enqueue chapter, taskAppend).
+    return launch_local_copy(c, sb, rb, count * esize, s);
+  }
+  RingArgs a;
+  fill_common(c, &a, sb, rb);
+  a.count = (int64_t)count;
+  const size_t per_rank_bytes = (mode == kAllReduce ? count : count * n) * esize;
+  bool flag = false;
+  fill_proto(c, &a, per_rank_bytes, esize, &flag);
+  // Vector moves need every unit to start on a 16-byte boundary; for the
+  // block-strided collectives that requires whole 16-byte blocks.
+  a.vec_ok = vec && (mode == kAllReduce || (count * esize) % 16 == 0);
+  const hipError_t e = flag ? launch_ring_flag(a, mode, dtype, op, s) : launch_ring_bulk(a, mode, dtype, op, s);
+  if (e != hipSuccess) {
+    RS_LOG(kLogWarn, "kernel launch failed: %s", hipGetErrorString(e));
+    return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  }
+  return RINGSIM_SUCCESS;
+}
+
+void free_comm_memory(ringsim_comm* c) {
+  if (c->fifo) (void)hipFree(c->fifo);
+  if (c->flag_fifo) (void)hipFree(c->flag_fifo);
+  if (c->ctr) (void)hipFree(c->ctr);
+  if (c->dev_abort) (void)hipFree(c->dev_abort);
+  if (c->host_words) (void)hipHostFree(c->host_words);
+  c->fifo = c->flag_fifo = nullptr;
+  c->ctr = nullptr;
+  c->dev_abort = nullptr;
+  c->host_words = c->host_words_dev = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+ringsim_result_t ringsim_config_default(ringsim_config_t* cfg) {
+  if (!cfg) return RINGSIM_INVALID_ARGUMENT;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->chunk_bytes = (size_t)env_long("RINGSIM_CHUNK_BYTES", 524288);
+  cfg->workgroups_per_channel = (int)env_long("RINGSIM_WPC", 0);
+  cfg->slot_bytes = (size_t)env_long("RINGSIM_SLOT_BYTES", kDefaultSlotBytes);
+  cfg->nslots = (int)env_long("RINGSIM_NSLOTS", kDefaultSlots);
+  cfg->timeout_ms = (int)env_long("RINGSIM_TIMEOUT_MS", 10000);
+  cfg->flag_threshold_bytes = (size_t)env_long("RINGSIM_FLAG_THRESHOLD", 65536);
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_comm_init(ringsim_comm_t* comm, int nranks, int nchannels, int proto) {
+  return ringsim_comm_init_config(comm, nranks, nchannels, proto, nullptr);
+}
+
+ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int nchannels, int proto,
+                                          const ringsim_config_t* user_cfg) {
+  if (!comm) return RINGSIM_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS) return RINGSIM_INVALID_ARGUMENT;
+  if (nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS) return RINGSIM_INVALID_ARGUMENT;
+  if (proto < RINGSIM_PROTO_AUTO || proto > RINGSIM_PROTO_FLAG) return RINGSIM_INVALID_ARGUMENT;
+  ringsim_config_t cfg;
+  ringsim_config_default(&cfg);
+  if (user_cfg) {
+    if (user_cfg->chunk_bytes) cfg.chunk_bytes = user_cfg->chunk_bytes;
+    if (user_cfg->workgroups_per_channel) cfg.workgroups_per_channel = user_cfg->workgroups_per_channel;
+    if (user_cfg->slot_bytes) cfg.slot_bytes = user_cfg->slot_bytes;
+    if (user_cfg->nslots) cfg.nslots = user_cfg->nslots;
+    if (user_cfg->timeout_ms) cfg.timeout_ms = user_cfg->timeout_ms;
+    if (user_cfg->flag_threshold_bytes) cfg.flag_threshold_bytes = user_cfg->flag_threshold_bytes;
+  }
+  if (cfg.chunk_bytes == 0 || cfg.chunk_bytes % 16 || cfg.chunk_bytes > ((size_t)1 << 30))
+    return RINGSIM_INVALID_ARGUMENT;
+  if (cfg.slot_bytes < 4096 || cfg.slot_bytes % 4096 || cfg.slot_bytes > ((size_t)1 << 22))
+    return RINGSIM_INVALID_ARGUMENT;
+  if (cfg.nslots < 2 || cfg.nslots > 4096) return RINGSIM_INVALID_ARGUMENT;
+  if (cfg.workgroups_per_channel < 0 || cfg.workgroups_per_channel > RINGSIM_MAX_WORKGROUPS_PER_CHANNEL)
+    return RINGSIM_INVALID_ARGUMENT;
+  if (cfg.timeout_ms <= 0) return RINGSIM_INVALID_ARGUMENT;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  int cus = 0, clock_khz = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || cus <= 0 ||
+      clock_khz <= 0)
+    return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  const int per_cu = ring_blocks_per_cu();
+  if (per_cu <= 0) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  const int64_t max_resident = (int64_t)per_cu * cus;
+
+  // Workgroups per channel: enough ring pipelines to give every CU two
+  // workgroups, but never more workgroups than can be resident at once (every
+  // workgroup of a launch spins on its neighbours).
+  const int64_t nc = (int64_t)nranks * nchannels;
+  if (nc > max_resident) return RINGSIM_INVALID_USAGE;
+  int wpc = cfg.workgroups_per_channel;
+  if (wpc == 0) wpc = (int)std::max<int64_t>(1, std::min<int64_t>(RINGSIM_MAX_WORKGROUPS_PER_CHANNEL,
+                                                                    (2 * (int64_t)cus) / nc));
+  while (wpc > 1 && nc * wpc > max_resident) --wpc;
+  if (nc * wpc > max_resident) return RINGSIM_INVALID_USAGE;
+
+  // FIFO depth: one stage of one workgroup may fill at most half of its FIFO,
+  // as NCCL's chunkSteps = NCCL_STEPS/2 ("NCCL" book, enqueue chapter,
+  // ALLREDUCE_CHUNKSTEPS). With every rank in stage 0 (sending only), a deeper
+  // stage could fill every FIFO of the ring at once and stall it.
+  const size_t stage_bytes = (size_t)align_up(div_up((int64_t)cfg.chunk_bytes, wpc), 16);
+  const int slices = (int)div_up((int64_t)stage_bytes, (int64_t)cfg.slot_bytes);
+  const int nslots = std::max(cfg.nslots, 2 * slices);
+
+  ringsim_comm* c = new (std::nothrow) ringsim_comm();
+  if (!c) return RINGSIM_SYSTEM_ERROR;
+  std::memset(c, 0, sizeof(*c));
+  c->nranks = nranks;
+  c->nchannels = nchannels;
+  c->proto = proto;
+  c->wpc = wpc;
+  c->nslots = nslots;
+  c->device = dev;
+  c->chunk_bytes = cfg.chunk_bytes;
+  c->slot_bytes = cfg.slot_bytes;
+  c->flag_threshold = cfg.flag_threshold_bytes;
+  c->timeout_ms = cfg.timeout_ms;
+  c->timeout_ticks = (uint64_t)cfg.timeout_ms * (uint64_t)clock_khz;
+  c->compute_units = cus;
+  c->blocks_per_cu = per_cu;
+  c->sticky = RINGSIM_SUCCESS;
+
+  const int64_t pipes = nc * wpc;
+  c->fifo_bytes = (size_t)pipes * nslots * cfg.slot_bytes;
+  c->flag_fifo_bytes = (size_t)nc * kFlagSlots * kFlagSlotBytes;
+  c->ctr_bytes = (size_t)pipes * sizeof(FifoCtr);
+  bool ok = hipMalloc((void**)&c->fifo, c->fifo_bytes) == hipSuccess &&
+            hipMalloc((void**)&c->flag_fifo, c->flag_fifo_bytes) == hipSuccess &&
+            hipMalloc((void**)&c->ctr, c->ctr_bytes) == hipSuccess &&
+            hipMalloc((void**)&c->dev_abort, 256) == hipSuccess &&
+            hipHostMalloc((void**)&c->host_words, 256, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
+  if (ok) ok = hipHostGetDevicePointer((void**)&c->host_words_dev, c->host_words, 0) == hipSuccess;
+  // Flags of the flag-packed FIFO start at zero, a value no step ever uses.
+  if (ok) ok = hipMemset(c->flag_fifo, 0, c->flag_fifo_bytes) == hipSuccess &&
+               hipMemset(c->ctr, 0, c->ctr_bytes) == hipSuccess && hipMemset(c->dev_abort, 0, 256) == hipSuccess &&
+               hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    free_comm_memory(c);
+    delete c;
+    (void)hipGetLastError();
+    return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  }
+  std::memset(c->host_words, 0, 256);
+  c->start_magic = kLiveMagic;
+  c->end_magic = kLiveMagic;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.insert(c);
+  }
+  RS_LOG(kLogInfo,
+         "comm %p: nranks %d nchannels %d proto %d wpc %d nslots %d slot %zu chunk %zu fifo %zu B flag fifo %zu B "
+         "resident %d/CU x %d CUs",
+         (void*)c, nranks, nchannels, proto, wpc, nslots, cfg.slot_bytes, cfg.chunk_bytes, c->fifo_bytes,
+         c->flag_fifo_bytes, per_cu, cus);
+  *comm = c;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_comm_destroy(ringsim_comm_t comm) {
+  ringsim_result_t res = check_comm(comm);
+  if (res != RINGSIM_SUCCESS) return res;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.erase(comm);
+  }
+  // Every kernel bounds its waits, so this returns even after an abort.
+  hipError_t e = comm->has_last_stream ? hipStreamSynchronize(comm->last_stream) : hipSuccess;
+  if (e != hipSuccess) e = hipDeviceSynchronize();
+  free_comm_memory(comm);
+  comm->start_magic = kDeadMagic;
+  comm->end_magic = kDeadMagic;
+  delete comm;
+  return e == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR;
+}
+
+ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* info) {
+  ringsim_result_t res = check_comm(comm);
+  if (res != RINGSIM_SUCCESS) return res;
+  if (!info) return RINGSIM_INVALID_ARGUMENT;
+  std::memset(info, 0, sizeof(*info));
+  info->nranks = comm->nranks;
+  info->nchannels = comm->nchannels;
+  info->proto = comm->proto;
+  info->workgroups_per_channel = comm->wpc;
+  info->nslots = comm->nslots;
+  info->device = comm->device;
+  info->chunk_bytes = comm->chunk_bytes;
+  info->slot_bytes = comm->slot_bytes;
+  info->flag_threshold_bytes = comm->flag_threshold;
+  info->fifo_bytes = comm->fifo_bytes;
+  info->flag_fifo_bytes = comm->flag_fifo_bytes;
+  info->max_resident_workgroups = comm->blocks_per_cu * comm->compute_units;
+  info->compute_units = comm->compute_units;
+  info->calls = comm->calls;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_allreduce(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                   size_t count, int dtype, int op, ringsim_stream_t stream) {
+  return run_ring(comm, kAllReduce, sendbufs, recvbufs, count, dtype, op, stream);
+}
+
+ringsim_result_t ringsim_reduce_scatter(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                        size_t recvcount, int dtype, int op, ringsim_stream_t stream) {
+  return run_ring(comm, kReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream);
+}
+
+ringsim_result_t ringsim_all_gather(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                    size_t sendcount, int dtype, ringsim_stream_t stream) {
+  return run_ring(comm, kAllGather, sendbufs, recvbufs, sendcount, dtype, RINGSIM_SUM, stream);
+}
+
+ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                                  size_t count, int dtype, ringsim_stream_t stream) {
+  ringsim_result_t res = check_comm(comm);
+  if (res != RINGSIM_SUCCESS) return res;
+  if ((res = poll_async(comm)) != RINGSIM_SUCCESS) return res;
+  if (!valid_dtype(dtype)) return RINGSIM_INVALID_ARGUMENT;
+  const int esize = dtype_size(dtype);
+  const int64_t n = comm->nranks;
+  if (count > (size_t)(INT64_MAX / 16) / (size_t)n / (size_t)esize) return RINGSIM_INVALID_ARGUMENT;
+  if (count == 0) return RINGSIM_SUCCESS;
+  bool vec = false;
+  if ((res = check_bufs(comm, sendbufs, recvbufs, esize, &vec)) != RINGSIM_SUCCESS) return res;
+  for (int r = 0; r < n; ++r)
+    if (sendbufs[r] == recvbufs[r]) return RINGSIM_INVALID_ARGUMENT;  // no in-place transpose
+  if ((res = check_device(comm)) != RINGSIM_SUCCESS) return res;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  comm->calls++;
+  comm->last_stream = s;
+  comm->has_last_stream = true;
+  CopyArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  for (int r = 0; r < n; ++r) {
+    ca.src[r] = static_cast<const char*>(sendbufs[r]);
+    ca.dst[r] = static_cast<char*>(recvbufs[r]);
+  }
+  ca.block_bytes = (int64_t)count * esize;
+  ca.nranks = (int)n;
+  ca.transpose = 1;
+  ca.vec_ok = vec && (ca.block_bytes % 16 == 0);
+  if (launch_copy(ca, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error) {
+  ringsim_result_t res = check_comm(comm);
+  if (res != RINGSIM_SUCCESS) return res;
+  if (!async_error) return RINGSIM_INVALID_ARGUMENT;
+  ringsim_result_t st = poll_async(comm);
+  if (st == RINGSIM_SUCCESS && comm->has_last_stream) {
+    const hipError_t q = hipStreamQuery(comm->last_stream);
+    if (q == hipErrorNotReady) {
+      st = RINGSIM_IN_PROGRESS;
+    } else if (q != hipSuccess) {
+      st = RINGSIM_UNHANDLED_DEVICE_ERROR;
+    } else {
+      st = poll_async(comm);  // the kernel may have just finished with an error
+    }
+  }
+  *async_error = st;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_abort(ringsim_comm_t comm) {
+  ringsim_result_t res = check_comm(comm);
+  if (res != RINGSIM_SUCCESS) return res;
+  __atomic_store_n(&comm->host_words[0], 1u, __ATOMIC_RELEASE);
+  comm->sticky = RINGSIM_ABORTED;
+  return RINGSIM_SUCCESS;
+}
+
+const char* ringsim_get_error_string(ringsim_result_t result) {
+  switch (result) {
+    case RINGSIM_SUCCESS: return "no error";
+    case RINGSIM_UNHANDLED_DEVICE_ERROR: return "unhandled device (HIP) error";
+    case RINGSIM_SYSTEM_ERROR: return "system error";
+    case RINGSIM_INTERNAL_ERROR: return "internal error: a ring kernel timed out waiting for a peer";
+    case RINGSIM_INVALID_ARGUMENT: return "invalid argument";
+    case RINGSIM_INVALID_USAGE: return "invalid usage";
+    case RINGSIM_IN_PROGRESS: return "operation in progress";
+    case RINGSIM_ABORTED: return "communicator aborted";
+    default: return "unknown result code";
+  }
+}
+
+ringsim_result_t ringsim_debug_plan(int coll, size_t count, int nranks, int nchannels, size_t chunk_bytes,
+                                    int dtype, int64_t* rows, size_t max_rows, size_t* nrows) {
+  if (!nrows || !valid_dtype(dtype)) return RINGSIM_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS)
+    return RINGSIM_INVALID_ARGUMENT;
+  if (chunk_bytes == 0 || chunk_bytes % 16) return RINGSIM_INVALID_ARGUMENT;
+  if (coll < RINGSIM_COLL_ALLREDUCE || coll > RINGSIM_COLL_ALL_GATHER) return RINGSIM_INVALID_ARGUMENT;
+  if (count > ((size_t)1 << 40)) return RINGSIM_INVALID_ARGUMENT;
+  const int64_t esize = dtype_size(dtype);
+  const int64_t A = 16 / esize;
+  const int64_t chunk = (int64_t)chunk_bytes / esize;
+  size_t k = 0;
+  auto emit = [&](int64_t c, int64_t l, int64_t ch, int64_t lo, int64_t hi) {
+    if (rows && k < max_rows) {
+      int64_t* row = rows + 5 * k;
+      row[0] = c;
+      row[1] = l;
+      row[2] = ch;
+      row[3] = lo;
+      row[4] = hi;
+    }
+    ++k;
+  };
+  for (int c = 0; c < nchannels; ++c) {
+    const Range chr = channel_range((int64_t)count, nchannels, c, A);
+    const int64_t L = chr.hi - chr.lo;
+    if (coll == RINGSIM_COLL_ALLREDUCE) {
+      const int64_t loop = (int64_t)nranks * chunk;
+      int64_t l = 0;
+      for (int64_t off = 0; off < L; off += loop, ++l) {
+        const int64_t rem = L - off;
+        const int64_t cur = ar_loop_chunk(rem, nranks, chunk, A);
+        for (int kk = 0; kk < nranks; ++kk) {
+          const Range r = ar_chunk(off, rem, cur, kk);
+          emit(c, l, kk, chr.lo + r.lo, chr.lo + r.hi);
+        }
+      }
+    } else {
+      int64_t l = 0;
+      for (int64_t off = 0; off < L; off += chunk, ++l) emit(c, l, -1, chr.lo + off, chr.lo + min64(off + chunk, L));
+    }
+  }
+  *nrows = k;
+  return RINGSIM_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// ringsim_internal.h -- structures shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ringsim.h"
+
+namespace ringsim {
+
+constexpr int kThreads = 256;         // threads per workgroup (4 wave64)
+constexpr int kUnroll = 8;            // 16-byte vectors in flight per thread
+constexpr int kDefaultSlotBytes = kThreads * 16 * kUnroll;  // 32 KiB: one pass per slot
+constexpr int kDefaultSlots = 8;      // FIFO depth (NCCL_STEPS)
+constexpr int kFlagLinesPerThread = 4;  // flag-packed: 16-byte lines per thread per slot
+constexpr int kFlagSlotBytes = kThreads * kFlagLinesPerThread * 16;  // 16 KiB (8 KiB payload)
+constexpr int kFlagSlots = 16;
+constexpr int kFlagHeadEvery = kFlagSlots / 2;  // flag path publishes head every this many steps
+// Largest chunk the flag path may use: one stage of a workgroup must fit in
+// the FIFO part that is always free while both neighbours sit in stage 0.
+constexpr int kFlagChunkBytes = (kFlagSlots - kFlagHeadEvery) * (kFlagSlotBytes / 2);  // 64 KiB
+
+// Step counters of one FIFO (sender -> receiver, pipeline). The producer owns
+// `tail` (slots filled), the consumer owns `head` (slots drained). Each sits
+// in its own 128-byte line so that the two sides never share a cache line
+// ("NCCL" book, s. 2.1 cache-line padding; s. 2.4 ncclSendMem/ncclRecvMem).
+struct alignas(256) FifoCtr {
+  uint64_t tail;
+  char pad0[120];
+  uint64_t head;
+  char pad1[120];
+};
+static_assert(sizeof(FifoCtr) == 256, "FifoCtr layout");
+
+enum Mode : int { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+
+// Error codes a kernel leaves in the host-visible error word.
+enum KernelError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrAborted = 2 };
+
+struct RingArgs {
+  const char* send[RINGSIM_MAX_RANKS];
+  char* recv[RINGSIM_MAX_RANKS];
+  int64_t count;        // all-reduce: per rank; reduce-scatter: recvcount; all-gather: sendcount
+  int64_t chunk;        // chunk elements (multiple of 16 bytes)
+  int nranks;
+  int nchannels;
+  int wpc;              // workgroups (pipelines) per channel in this launch
+  int pipe_stride;      // pipelines per rank in the counter array
+  int pipe_mul;         // counter pipeline of (channel c, part w) = c * pipe_mul + w
+  int fifo_stride;      // pipelines per rank in the FIFO array of this protocol
+  int fifo_mul;         // FIFO pipeline of (channel c, part w) = c * fifo_mul + w
+  int nslots;
+  int slot_bytes;
+  int vec_ok;           // every user buffer is 16-byte aligned
+  char* fifo;           // FIFO slots: [rank][pipeline][slot][slot_bytes]
+  FifoCtr* ctr;         // counters: [rank][pipeline]
+  uint32_t* dev_abort;  // device word: set when any workgroup gives up
+  const uint32_t* host_abort;  // host-mapped word set by ringsim_abort
+  uint32_t* host_err;   // host-mapped error word
+  uint64_t timeout_ticks;  // bound on one wait, in wall-clock ticks
+};
+
+struct CopyArgs {
+  const char* src[RINGSIM_MAX_RANKS];
+  char* dst[RINGSIM_MAX_RANKS];
+  int64_t block_bytes;  // bytes of one (source rank, destination rank) block
+  int nranks;
+  int transpose;        // 1: all-to-all; 0: rank r copies src[r] -> dst[r]
+  int vec_ok;
+};
+
+// Kernel launchers (ringsim_kernels.hip).
+hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
+hipError_t launch_ring_flag(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+// Max co-resident workgroups per CU over every ring kernel instantiation.
+int ring_blocks_per_cu();
+
+inline int dtype_size(int dtype) {
+  switch (dtype) {
+    case RINGSIM_INT32: return 4;
+    case RINGSIM_INT64: return 8;
+    case RINGSIM_FLOAT32: return 4;
+    case RINGSIM_BFLOAT16: return 2;
+    default: return 0;
+  }
+}
+
+}  // namespace ringsim

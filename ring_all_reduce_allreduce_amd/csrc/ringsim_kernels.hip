@@ -1,0 +1,753 @@
+// ringsim_kernels.hip -- ring collective kernels for CDNA4 (gfx950).
+//
+// One launch runs a whole collective. Workgroup (r, p) plays simulated rank r
+// on pipeline p = (channel c, part w): it walks the ring schedule of its
+// channel and, at every stage, moves its part of the stage's chunk through the
+// FIFO from rank r-1 into the FIFO to rank r+1, reducing with rank r's own
+// data on the way ("NCCL" book, aireadcode.com, ch. 2, s. 2.2 channels,
+// s. 2.3 RingARAlgorithm, s. 2.4 protocols). The workgroups of one pipeline
+// form a ring of producer/consumer pairs; workgroup ids are rank-major so
+// that, when the pipeline count is a multiple of 8, every workgroup of a
+// pipeline is dispatched to the same XCD and its FIFO traffic stays behind
+// one L2.
+//
+// Two protocols:
+//   bulk  FIFO slots hold raw payload; readiness travels in separate 64-bit
+//         step counters (tail: slots filled, head: slots drained), published
+//         with agent-scope release after the slot's stores complete and read
+//         with agent-scope acquire before the slot is read (Simple).
+//   flag  FIFO lines of 16 bytes carry two {4-byte payload, 4-byte flag}
+//         words; each 8-byte word is written and read as one 64-bit access,
+//         so a receiver that sees the expected flag also sees its payload.
+//         No fences on the data path; head is published every few steps for
+//         flow control only (LL).
+// Every wait is bounded: a workgroup that waits longer than the timeout, or
+// sees the abort word, records an error and stops waiting; the launch then
+// runs to completion with undefined payload, and the host reports the error.
+#include <hip/hip_runtime.h>
+
+#include "ring_plan.h"
+#include "ringsim_internal.h"
+
+namespace ringsim {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Element operators (one hop, rounded to the buffer type)
+// ---------------------------------------------------------------------------
+
+template <int OP>
+__device__ __forceinline__ float op_f32(float a, float b) {
+  if constexpr (OP == RINGSIM_SUM) {
+    return a + b;
+  } else if constexpr (OP == RINGSIM_PROD) {
+    return a * b;
+  } else if constexpr (OP == RINGSIM_MAX) {
+    if (a > b) return a;
+    if (b > a) return b;
+    return __uint_as_float(__float_as_uint(a) & __float_as_uint(b));  // max(+0,-0) = +0
+  } else {
+    if (a < b) return a;
+    if (b < a) return b;
+    return __uint_as_float(__float_as_uint(a) | __float_as_uint(b));  // min(+0,-0) = -0
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t op_i32(uint32_t a, uint32_t b) {
+  if constexpr (OP == RINGSIM_SUM) {
+    return a + b;
+  } else if constexpr (OP == RINGSIM_PROD) {
+    return a * b;
+  } else if constexpr (OP == RINGSIM_MAX) {
+    return (int32_t)a > (int32_t)b ? a : b;
+  } else {
+    return (int32_t)a < (int32_t)b ? a : b;
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ uint64_t op_i64(uint64_t a, uint64_t b) {
+  if constexpr (OP == RINGSIM_SUM) {
+    return a + b;
+  } else if constexpr (OP == RINGSIM_PROD) {
+    return a * b;
+  } else if constexpr (OP == RINGSIM_MAX) {
+    return (int64_t)a > (int64_t)b ? a : b;
+  } else {
+    return (int64_t)a < (int64_t)b ? a : b;
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two bf16 values packed in a 32-bit word: each computed in fp32, rounded once.
+template <int OP>
+__device__ __forceinline__ uint32_t op_bf16x2(uint32_t a, uint32_t b) {
+  const uint32_t lo = to_bf16(op_f32<OP>(bf16_lo(a), bf16_lo(b)));
+  const uint32_t hi = to_bf16(op_f32<OP>(bf16_hi(a), bf16_hi(b)));
+  return lo | (hi << 16);
+}
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<RINGSIM_INT32> { using T = uint32_t; };
+template <>
+struct Elem<RINGSIM_INT64> { using T = uint64_t; };
+template <>
+struct Elem<RINGSIM_FLOAT32> { using T = uint32_t; };
+template <>
+struct Elem<RINGSIM_BFLOAT16> { using T = uint16_t; };
+
+// Reduction on 4-, 8- and 16-byte packets and on single elements.
+template <int DT, int OP>
+struct VOp {
+  using T = typename Elem<DT>::T;
+
+  static __device__ __forceinline__ uint32_t word(uint32_t a, uint32_t b) {
+    if constexpr (DT == RINGSIM_FLOAT32) {
+      return __float_as_uint(op_f32<OP>(__uint_as_float(a), __uint_as_float(b)));
+    } else if constexpr (DT == RINGSIM_INT32) {
+      return op_i32<OP>(a, b);
+    } else {
+      return op_bf16x2<OP>(a, b);
+    }
+  }
+
+  static __device__ __forceinline__ u32x2 v2(u32x2 a, u32x2 b) {
+    if constexpr (DT == RINGSIM_INT64) {
+      const uint64_t x = ((uint64_t)a.y << 32) | a.x;
+      const uint64_t y = ((uint64_t)b.y << 32) | b.x;
+      const uint64_t z = op_i64<OP>(x, y);
+      return u32x2{(uint32_t)z, (uint32_t)(z >> 32)};
+    } else {
+      return u32x2{word(a.x, b.x), word(a.y, b.y)};
+    }
+  }
+
+  static __device__ __forceinline__ u32x4 v4(u32x4 a, u32x4 b) {
+    const u32x2 lo = v2(u32x2{a.x, a.y}, u32x2{b.x, b.y});
+    const u32x2 hi = v2(u32x2{a.z, a.w}, u32x2{b.z, b.w});
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+  }
+
+  static __device__ __forceinline__ T one(T a, T b) {
+    if constexpr (DT == RINGSIM_INT64) {
+      return op_i64<OP>(a, b);
+    } else if constexpr (DT == RINGSIM_BFLOAT16) {
+      return (T)to_bf16(op_f32<OP>(bf16_lo(a), bf16_lo(b)));
+    } else {
+      return word(a, b);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Synchronisation helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+// Wait until every global load and store this thread issued has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// What a waiting thread needs to give up cleanly; kept small so that it
+// lives in registers rather than copying the kernel arguments.
+struct WaitCtx {
+  uint32_t* dev_abort;
+  const uint32_t* host_abort;
+  uint32_t* host_err;
+  uint64_t timeout_ticks;
+};
+
+__device__ __forceinline__ WaitCtx wait_ctx(const RingArgs& a) {
+  return WaitCtx{a.dev_abort, a.host_abort, a.host_err, a.timeout_ticks};
+}
+
+__device__ __forceinline__ bool host_abort_seen(const WaitCtx& w) {
+  return __hip_atomic_load(w.host_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u;
+}
+
+__device__ __forceinline__ bool abort_seen(const WaitCtx& w) {
+  return __hip_atomic_load(w.dev_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || host_abort_seen(w);
+}
+
+// Records the first error in the host-visible word and tells every other
+// workgroup of the launch to stop waiting.
+__device__ __forceinline__ void raise_error(WaitCtx w, uint32_t code) {
+  atomicCAS_system(w.host_err, 0u, code);
+  __hip_atomic_store(w.dev_abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Checked every 256 spins: abort word, then the time bound.
+__device__ __forceinline__ bool give_up(const WaitCtx& w, uint64_t t0) {
+  if (abort_seen(w)) {
+    raise_error(w, host_abort_seen(w) ? kErrAborted : kErrTimeout);
+    return true;
+  }
+  if (wall_clock64() - t0 > w.timeout_ticks) {
+    raise_error(w, kErrTimeout);
+    return true;
+  }
+  return false;
+}
+
+// Spins until *p >= target and returns the value seen, or returns 0 (never a
+// valid answer: targets start at 1) after recording why it gave up.
+__device__ __forceinline__ uint64_t wait_geq(const uint64_t* p, uint64_t target, WaitCtx w) {
+  uint64_t v = ld_relaxed(p);
+  if (v >= target) return v;
+  if (abort_seen(w)) {
+    raise_error(w, host_abort_seen(w) ? kErrAborted : kErrTimeout);
+    return 0;
+  }
+  const uint64_t t0 = wall_clock64();
+  uint32_t it = 0;
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_relaxed(p);
+    if (v >= target) return v;
+    if ((++it & 255u) == 0u && give_up(w, t0)) return 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bulk data movement: one FIFO slot worth of a unit
+// ---------------------------------------------------------------------------
+
+// Whole 16-byte vectors: x = RED ? op(src, loc) : src, then x -> fout and/or
+// uout. Full tiles run unguarded so that all loads of a tile are in flight
+// before the first use; the last partial tile is guarded.
+template <int DT, int OP, bool RED, bool FOUT, bool UOUT>
+__device__ __forceinline__ void move_vec(int64_t nv, const u32x4* __restrict__ src, const u32x4* __restrict__ l4,
+                                         u32x4* __restrict__ f4, u32x4* __restrict__ u4) {
+  const int tid = threadIdx.x;
+  constexpr int64_t kTile = (int64_t)kThreads * kUnroll;
+  int64_t base = 0;
+  for (; base + kTile <= nv; base += kTile) {
+    u32x4 v[kUnroll];
+    u32x4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = src[base + u * kThreads + tid];
+    if constexpr (RED) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) x[u] = l4[base + u * kThreads + tid];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = VOp<DT, OP>::v4(v[u], x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (FOUT) f4[base + u * kThreads + tid] = v[u];
+      if constexpr (UOUT) u4[base + u * kThreads + tid] = v[u];
+    }
+  }
+  for (int64_t i = base + tid; i < nv; i += kThreads) {
+    u32x4 v = src[i];
+    if constexpr (RED) v = VOp<DT, OP>::v4(v, l4[i]);
+    if constexpr (FOUT) f4[i] = v;
+    if constexpr (UOUT) u4[i] = v;
+  }
+}
+
+// One FIFO slot worth of a unit: x = fin ? (loc ? op(fin, loc) : fin) : loc,
+// then x -> fout and/or uout. fin/fout are FIFO slots (16-byte aligned);
+// loc/uout are user data, vector-moved only when vec_ok.
+template <int DT, int OP>
+__device__ __forceinline__ void move_slice(int64_t n, const char* fin, const char* loc, char* fout, char* uout,
+                                           int vec_ok) {
+  using T = typename Elem<DT>::T;
+  constexpr int A = 16 / (int)sizeof(T);
+  const int64_t nv = vec_ok ? n / A : 0;
+  if (nv > 0) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(fin ? fin : loc);
+    const u32x4* l4 = reinterpret_cast<const u32x4*>(loc);
+    u32x4* f4 = reinterpret_cast<u32x4*>(fout);
+    u32x4* u4 = reinterpret_cast<u32x4*>(uout);
+    if (fin && loc) {
+      if (fout && uout) move_vec<DT, OP, true, true, true>(nv, src, l4, f4, u4);
+      else if (fout) move_vec<DT, OP, true, true, false>(nv, src, l4, f4, u4);
+      else move_vec<DT, OP, true, false, true>(nv, src, l4, f4, u4);
+    } else {
+      if (fout && uout) move_vec<DT, OP, false, true, true>(nv, src, l4, f4, u4);
+      else if (fout) move_vec<DT, OP, false, true, false>(nv, src, l4, f4, u4);
+      else move_vec<DT, OP, false, false, true>(nv, src, l4, f4, u4);
+    }
+  }
+  // Elements past the last whole vector (or all of them when user buffers
+  // are not 16-byte aligned).
+  const T* s1 = reinterpret_cast<const T*>(fin ? fin : loc);
+  const T* l1 = (fin && loc) ? reinterpret_cast<const T*>(loc) : nullptr;
+  T* f1 = reinterpret_cast<T*>(fout);
+  T* o1 = reinterpret_cast<T*>(uout);
+  for (int64_t i = nv * A + threadIdx.x; i < n; i += kThreads) {
+    T x = s1[i];
+    if (l1) x = VOp<DT, OP>::one(x, l1[i]);
+    if (f1) f1[i] = x;
+    if (o1) o1[i] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Schedule walker: calls unit(m, recv, use_local, send, store, local, out)
+// for every unit of workgroup (r, c, w) in FIFO order.
+// ---------------------------------------------------------------------------
+
+template <int DT, int MODE, typename Unit>
+__device__ __forceinline__ void walk(const RingArgs& a, int r, int c, int w, Unit&& unit) {
+  using T = typename Elem<DT>::T;
+  constexpr int64_t E = sizeof(T);
+  constexpr int64_t A = 16 / E;
+  const int N = a.nranks;
+  const Range ch = channel_range(a.count, a.nchannels, c, A);
+  const int64_t L = ch.hi - ch.lo;
+  if constexpr (MODE == kAllReduce) {
+    // "NCCL" book s. 2.3: a loop covers N chunks; stage j of rank r visits
+    // chunk (r + N - 1 - j) mod N: stages 0..N-1 reduce-scatter (stage N-1
+    // completes chunk r), stages N-1..2N-2 store, stages 0..2N-3 forward.
+    const int64_t loop = (int64_t)N * a.chunk;
+    for (int64_t off = 0; off < L; off += loop) {
+      const int64_t rem = L - off;
+      const int64_t cur = ar_loop_chunk(rem, N, a.chunk, A);
+      for (int j = 0; j < 2 * N - 1; ++j) {
+        const Range ck = ar_chunk(off, rem, cur, ring_chunk(r, N, j));
+        const Range pt = split_part(ck.hi - ck.lo, a.wpc, w, A);
+        const int64_t e0 = ch.lo + ck.lo + pt.lo;
+        unit(pt.hi - pt.lo, j >= 1, j <= N - 1, j <= 2 * N - 3, j >= N - 1, a.send[r] + e0 * E,
+             a.recv[r] + e0 * E);
+      }
+    }
+  } else if constexpr (MODE == kReduceScatter) {
+    // Block b is folded b+1, ..., b and lands on rank b (stage N-1).
+    for (int64_t off = 0; off < L; off += a.chunk) {
+      const int64_t cur = min64(a.chunk, L - off);
+      const Range pt = split_part(cur, a.wpc, w, A);
+      const int64_t e0 = ch.lo + off + pt.lo;
+      for (int j = 0; j < N; ++j) {
+        const int k = ring_chunk(r, N, j);
+        unit(pt.hi - pt.lo, j >= 1, true, j <= N - 2, j == N - 1, a.send[r] + ((int64_t)k * a.count + e0) * E,
+             a.recv[r] + e0 * E);
+      }
+    }
+  } else {
+    // All-gather, "NCCL 专家课程 17" (Bootstrap Ring 与 AllGather): round j
+    // sends block (r - j) and receives block (r - j - 1).
+    for (int64_t off = 0; off < L; off += a.chunk) {
+      const int64_t cur = min64(a.chunk, L - off);
+      const Range pt = split_part(cur, a.wpc, w, A);
+      const int64_t e0 = ch.lo + off + pt.lo;
+      for (int j = 0; j < N; ++j) {
+        const int b = ag_block(r, N, j);
+        unit(pt.hi - pt.lo, j >= 1, j == 0, j <= N - 2, true, a.send[r] + e0 * E,
+             a.recv[r] + ((int64_t)b * a.count + e0) * E);
+      }
+    }
+  }
+}
+
+struct Pipe {
+  int r, c, w, pipe;
+  FifoCtr* in_ctr;
+  FifoCtr* out_ctr;
+  char* in_fifo;
+  char* out_fifo;
+};
+
+__device__ __forceinline__ Pipe locate(const RingArgs& a) {
+  Pipe p;
+  const int P = a.nchannels * a.wpc;
+  const int b = blockIdx.x;
+  p.r = b / P;
+  const int pl = b - p.r * P;
+  p.c = pl / a.wpc;
+  p.w = pl - p.c * a.wpc;
+  p.pipe = p.c * a.pipe_mul + p.w;
+  const int nxt = p.r + 1 == a.nranks ? 0 : p.r + 1;
+  p.in_ctr = a.ctr + (int64_t)p.r * a.pipe_stride + p.pipe;
+  p.out_ctr = a.ctr + (int64_t)nxt * a.pipe_stride + p.pipe;
+  const int fpipe = p.c * a.fifo_mul + p.w;
+  const int64_t fifo_bytes = (int64_t)a.nslots * a.slot_bytes;
+  p.in_fifo = a.fifo + ((int64_t)p.r * a.fifo_stride + fpipe) * fifo_bytes;
+  p.out_fifo = a.fifo + ((int64_t)nxt * a.fifo_stride + fpipe) * fifo_bytes;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Bulk kernel
+// ---------------------------------------------------------------------------
+
+template <int DT, int OP, int MODE>
+__global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int64_t E = sizeof(T);
+  const Pipe p = locate(a);
+  __shared__ uint64_t s_base[2];
+  if (threadIdx.x == 0) {
+    // Each side's own counter tells where the previous call left this FIFO.
+    s_base[0] = ld_relaxed(&p.in_ctr->head);
+    s_base[1] = ld_relaxed(&p.out_ctr->tail);
+  }
+  __syncthreads();
+  const uint64_t in_base = s_base[0];
+  const uint64_t out_base = s_base[1];
+  const uint64_t nslots = (uint64_t)a.nslots;
+  const int64_t slice = a.slot_bytes / E;
+  uint64_t nrecv = 0, nsent = 0;
+  uint64_t known_tail = 0, known_head = 0;  // meaningful in thread 0 only
+  bool stop = false;                         // thread 0: stop waiting
+  const WaitCtx wc = wait_ctx(a);
+
+  walk<DT, MODE>(a, p.r, p.c, p.w,
+                 [&](int64_t m, bool recv, bool use_local, bool send, bool store, const char* local, char* out) {
+    for (int64_t s = 0; s < m; s += slice) {
+      const int64_t ns = min64(slice, m - s);
+      if (threadIdx.x == 0 && !stop) {
+        // A value already seen (and acquired) may cover this step; otherwise
+        // poll, then acquire so that the producer's slot stores (or the
+        // consumer's drained-slot loads) are ordered before what follows.
+        bool fresh = false;
+        const uint64_t need_tail = in_base + nrecv + 1;
+        if (recv && known_tail < need_tail) {
+          known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
+          stop = known_tail == 0;
+          fresh = true;
+        }
+        const uint64_t need_head = out_base + nsent + 1 - nslots;
+        if (!stop && send && nsent + 1 > nslots && known_head < need_head) {
+          known_head = wait_geq(&p.out_ctr->head, need_head, wc);
+          stop = known_head == 0;
+          fresh = true;
+        }
+        if (fresh) fence_acquire();
+      }
+      __syncthreads();
+      const char* fin = recv ? p.in_fifo + ((in_base + nrecv) % nslots) * a.slot_bytes : nullptr;
+      char* fout = send ? p.out_fifo + ((out_base + nsent) % nslots) * a.slot_bytes : nullptr;
+      move_slice<DT, OP>(ns, fin, use_local ? local + s * E : nullptr, fout, store ? out + s * E : nullptr,
+                         a.vec_ok);
+      wait_vmem();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        fence_release();
+        if (send) st_relaxed(&p.out_ctr->tail, out_base + nsent + 1);
+        if (recv) st_relaxed(&p.in_ctr->head, in_base + nrecv + 1);
+      }
+      nrecv += recv ? 1 : 0;
+      nsent += send ? 1 : 0;
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Flag-packed kernel
+// ---------------------------------------------------------------------------
+
+// 16-byte line: {payload word 0, flag, payload word 1, flag}; each 8-byte
+// half is read as one 64-bit access, so a matching flag vouches for the word
+// stored with it.
+__device__ __forceinline__ u32x2 poll_line(const uint64_t* line, uint32_t flag, bool& stop, const WaitCtx& w) {
+  uint64_t v0 = ld_relaxed(line);
+  uint64_t v1 = ld_relaxed(line + 1);
+  if (!stop && ((uint32_t)(v0 >> 32) != flag || (uint32_t)(v1 >> 32) != flag)) {
+    const uint64_t t0 = wall_clock64();
+    uint32_t it = 0;
+    while ((uint32_t)(v0 >> 32) != flag || (uint32_t)(v1 >> 32) != flag) {
+      if ((++it & 255u) == 0u && give_up(w, t0)) {
+        stop = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v0 = ld_relaxed(line);
+      v1 = ld_relaxed(line + 1);
+    }
+  }
+  return u32x2{(uint32_t)v0, (uint32_t)v1};
+}
+
+template <int DT>
+__device__ __forceinline__ u32x2 load_payload(const char* p, int valid, int vec_ok) {
+  using T = typename Elem<DT>::T;
+  if (valid == 8 && vec_ok) return *reinterpret_cast<const u32x2*>(p);
+  union {
+    u32x2 v;
+    T e[8 / sizeof(T)];
+  } u;
+  u.v = u32x2{0u, 0u};
+#pragma unroll
+  for (int q = 0; q < (int)(8 / sizeof(T)); ++q)
+    if (q * (int)sizeof(T) < valid) u.e[q] = reinterpret_cast<const T*>(p)[q];
+  return u.v;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_payload(char* p, u32x2 x, int valid, int vec_ok) {
+  using T = typename Elem<DT>::T;
+  if (valid == 8 && vec_ok) {
+    *reinterpret_cast<u32x2*>(p) = x;
+    return;
+  }
+  union {
+    u32x2 v;
+    T e[8 / sizeof(T)];
+  } u;
+  u.v = x;
+#pragma unroll
+  for (int q = 0; q < (int)(8 / sizeof(T)); ++q)
+    if (q * (int)sizeof(T) < valid) reinterpret_cast<T*>(p)[q] = u.e[q];
+}
+
+template <int DT, int OP, int MODE>
+__global__ void __launch_bounds__(kThreads) ring_flag_kernel(RingArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int64_t E = sizeof(T);
+  const Pipe p = locate(a);
+  __shared__ uint64_t s_base[2];
+  __shared__ uint64_t s_head;
+  if (threadIdx.x == 0) {
+    s_base[0] = ld_relaxed(&p.in_ctr->head);
+    s_base[1] = ld_relaxed(&p.out_ctr->tail);
+  }
+  __syncthreads();
+  const uint64_t in_base = s_base[0];
+  const uint64_t out_base = s_base[1];
+  const uint64_t nslots = (uint64_t)a.nslots;
+  const int64_t slice = (a.slot_bytes / 2) / E;  // payload bytes per slot / element size
+  uint64_t nrecv = 0, nsent = 0;
+  uint64_t head_known = out_base;  // uniform across the workgroup
+  uint64_t known_head = 0;         // thread 0
+  bool stop = false;               // per thread: stop waiting
+  const WaitCtx wc = wait_ctx(a);
+
+  walk<DT, MODE>(a, p.r, p.c, p.w,
+                 [&](int64_t m, bool recv, bool use_local, bool send, bool store, const char* local, char* out) {
+    for (int64_t s = 0; s < m; s += slice) {
+      const int64_t ns = min64(slice, m - s);
+      if (send && nsent + 1 > nslots) {
+        const uint64_t need = out_base + nsent + 1 - nslots;
+        if (head_known < need) {  // uniform branch
+          if (threadIdx.x == 0) {
+            if (!stop && known_head < need) {
+              known_head = wait_geq(&p.out_ctr->head, need, wc);
+              stop = known_head == 0;
+            }
+            s_head = known_head > need ? known_head : need;
+          }
+          __syncthreads();
+          head_known = s_head;
+          __syncthreads();
+        }
+      }
+      const uint32_t flag_in = (uint32_t)(in_base + nrecv + 1);
+      const uint32_t flag_out = (uint32_t)(out_base + nsent + 1);
+      const uint64_t* fin =
+          recv ? reinterpret_cast<const uint64_t*>(p.in_fifo + ((in_base + nrecv) % nslots) * a.slot_bytes) : nullptr;
+      uint64_t* fout =
+          send ? reinterpret_cast<uint64_t*>(p.out_fifo + ((out_base + nsent) % nslots) * a.slot_bytes) : nullptr;
+      const int64_t nbytes = ns * E;
+      const int64_t nlines = div_up(nbytes, 8);
+      const char* lp = use_local ? local + s * E : nullptr;
+      char* op = store ? out + s * E : nullptr;
+      for (int64_t li = threadIdx.x; li < nlines; li += kThreads) {
+        const int64_t bo = li * 8;
+        const int valid = (int)min64(8, nbytes - bo);
+        u32x2 loc = u32x2{0u, 0u};
+        if (lp) loc = load_payload<DT>(lp + bo, valid, a.vec_ok);
+        u32x2 x;
+        if (fin) {
+          x = poll_line(fin + 2 * li, flag_in, stop, wc);
+          if (lp) x = VOp<DT, OP>::v2(x, loc);
+        } else {
+          x = loc;
+        }
+        if (fout) {
+          st_relaxed(fout + 2 * li, ((uint64_t)flag_out << 32) | x.x);
+          st_relaxed(fout + 2 * li + 1, ((uint64_t)flag_out << 32) | x.y);
+        }
+        if (op) store_payload<DT>(op + bo, x, valid, a.vec_ok);
+      }
+      nrecv += recv ? 1 : 0;
+      nsent += send ? 1 : 0;
+      if (recv && nrecv % kFlagHeadEvery == 0) {  // uniform: release drained slots
+        __syncthreads();
+        if (threadIdx.x == 0) st_relaxed(&p.in_ctr->head, in_base + nrecv);
+      }
+    }
+  });
+  // Leave both counters at the number of steps this call moved, so the next
+  // call (either protocol) starts from the same base on both sides.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st_relaxed(&p.in_ctr->head, in_base + nrecv);
+    st_relaxed(&p.out_ctr->tail, out_base + nsent);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Copy kernel: all-to-all blocks, or one-rank local copies
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
+  const int blk = blockIdx.y;
+  int src_rank, dst_rank;
+  int64_t src_off = 0, dst_off = 0;
+  if (a.transpose) {
+    dst_rank = blk / a.nranks;
+    src_rank = blk - dst_rank * a.nranks;
+    src_off = (int64_t)dst_rank * a.block_bytes;
+    dst_off = (int64_t)src_rank * a.block_bytes;
+  } else {
+    src_rank = dst_rank = blk;
+  }
+  const char* src = a.src[src_rank] + src_off;
+  char* dst = a.dst[dst_rank] + dst_off;
+  const int tid = threadIdx.x;
+  if (a.vec_ok) {
+    const int64_t nv = a.block_bytes / 16;
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+    const int64_t tile = (int64_t)kThreads * kUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * tile; base < nv; base += (int64_t)gridDim.x * tile) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = base + (int64_t)u * kThreads + tid;
+        if (i < nv) v[u] = __builtin_nontemporal_load(s4 + i);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = base + (int64_t)u * kThreads + tid;
+        if (i < nv) __builtin_nontemporal_store(v[u], d4 + i);
+      }
+    }
+    for (int64_t i = nv * 16 + (int64_t)blockIdx.x * kThreads + tid; i < a.block_bytes;
+         i += (int64_t)gridDim.x * kThreads)
+      dst[i] = src[i];
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.block_bytes; i += (int64_t)gridDim.x * kThreads)
+      dst[i] = src[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+
+template <int DT, int OP, int MODE>
+static hipError_t launch_bulk_t(const RingArgs& a, hipStream_t s) {
+  const int grid = a.nranks * a.nchannels * a.wpc;
+  hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int OP, int MODE>
+static hipError_t launch_flag_t(const RingArgs& a, hipStream_t s) {
+  const int grid = a.nranks * a.nchannels * a.wpc;
+  hipLaunchKernelGGL((ring_flag_kernel<DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool FLAG, int DT, int OP, int MODE>
+static hipError_t launch_t(const RingArgs& a, hipStream_t s) {
+  if constexpr (FLAG) return launch_flag_t<DT, OP, MODE>(a, s);
+  else return launch_bulk_t<DT, OP, MODE>(a, s);
+}
+
+template <bool FLAG, int DT, int MODE>
+static hipError_t dispatch_op(const RingArgs& a, int op, hipStream_t s) {
+  if constexpr (MODE == kAllGather) {
+    (void)op;
+    return launch_t<FLAG, DT, RINGSIM_SUM, MODE>(a, s);
+  } else {
+    switch (op) {
+      case RINGSIM_SUM: return launch_t<FLAG, DT, RINGSIM_SUM, MODE>(a, s);
+      case RINGSIM_PROD: return launch_t<FLAG, DT, RINGSIM_PROD, MODE>(a, s);
+      case RINGSIM_MAX: return launch_t<FLAG, DT, RINGSIM_MAX, MODE>(a, s);
+      case RINGSIM_MIN: return launch_t<FLAG, DT, RINGSIM_MIN, MODE>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+template <bool FLAG, int MODE>
+static hipError_t dispatch_dtype(const RingArgs& a, int dtype, int op, hipStream_t s) {
+  switch (dtype) {
+    case RINGSIM_INT32: return dispatch_op<FLAG, RINGSIM_INT32, MODE>(a, op, s);
+    case RINGSIM_INT64: return dispatch_op<FLAG, RINGSIM_INT64, MODE>(a, op, s);
+    case RINGSIM_FLOAT32: return dispatch_op<FLAG, RINGSIM_FLOAT32, MODE>(a, op, s);
+    case RINGSIM_BFLOAT16: return dispatch_op<FLAG, RINGSIM_BFLOAT16, MODE>(a, op, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool FLAG>
+static hipError_t dispatch_mode(const RingArgs& a, int mode, int dtype, int op, hipStream_t s) {
+  switch (mode) {
+    case kAllReduce: return dispatch_dtype<FLAG, kAllReduce>(a, dtype, op, s);
+    case kReduceScatter: return dispatch_dtype<FLAG, kReduceScatter>(a, dtype, op, s);
+    case kAllGather: return dispatch_dtype<FLAG, kAllGather>(a, dtype, op, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s) {
+  return dispatch_mode<false>(a, mode, dtype, op, s);
+}
+
+hipError_t launch_ring_flag(const RingArgs& a, int mode, int dtype, int op, hipStream_t s) {
+  return dispatch_mode<true>(a, mode, dtype, op, s);
+}
+
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
+  const int nblocks = a.transpose ? a.nranks * a.nranks : a.nranks;
+  const int64_t tile = a.vec_ok ? (int64_t)kThreads * kUnroll * 16 : (int64_t)kThreads;
+  int64_t tiles = div_up(a.block_bytes, tile);
+  const int64_t cap = max64(1, 4096 / nblocks);
+  if (tiles > cap) tiles = cap;
+  if (tiles < 1) tiles = 1;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)tiles, (unsigned)nblocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename K>
+static int occ(K k) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess) return 0;
+  return n;
+}
+
+int ring_blocks_per_cu() {
+  int m = 1 << 30;
+  auto acc = [&](int v) { m = v < m ? v : m; };
+#define RS_OCC_DT(DT)                                                                 \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce>));                            \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_MAX, kAllReduce>));                            \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_PROD, kReduceScatter>));                       \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_SUM, kAllGather>));                            \
+  acc(occ(ring_flag_kernel<DT, RINGSIM_SUM, kAllReduce>));                            \
+  acc(occ(ring_flag_kernel<DT, RINGSIM_MIN, kReduceScatter>));                        \
+  acc(occ(ring_flag_kernel<DT, RINGSIM_SUM, kAllGather>));
+  RS_OCC_DT(RINGSIM_INT32)
+  RS_OCC_DT(RINGSIM_INT64)
+  RS_OCC_DT(RINGSIM_FLOAT32)
+  RS_OCC_DT(RINGSIM_BFLOAT16)
+#undef RS_OCC_DT
+  return m == (1 << 30) ? 0 : m;
+}
+
+}  // namespace ringsim

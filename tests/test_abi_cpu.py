@@ -1,0 +1,118 @@
+"""Host-side checks of libringsim that need no GPU: the shared library loads,
+exports every function include/ringsim.h declares, plans exactly the ranges
+the oracle's independent partition gives, and follows the error conventions
+for bad arguments and bad handles."""
+import ctypes
+import itertools
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import ring_all_reduce_allreduce_amd as rs
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rs.LIB_PATH):
+        from ring_all_reduce_allreduce_amd import build
+
+        build.build()
+    return rs.lib()
+
+
+def test_exports_every_declared_function(L):
+    declared = rs.header_exports()
+    assert len(declared) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], check=True, capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(L, f)
+
+
+def test_error_strings(L):
+    for code in (0, 1, 2, 3, 4, 5, 7, 8):
+        assert rs.error_string(code)
+    assert rs.error_string(5) == "invalid usage"
+
+
+def _oracle_rows(coll, count, n, c, chunk_bytes, dtype):
+    a = 16 // oracle.ELEM_SIZE[dtype]
+    chunk = chunk_bytes // oracle.ELEM_SIZE[dtype]
+    rows = []
+    for ci, (lo, hi) in enumerate(oracle.channel_ranges(count, c, a)):
+        if coll == "allreduce":
+            for l, ks in enumerate(oracle.allreduce_loop_chunks(hi - lo, n, chunk, a)):
+                for k, (b, e) in enumerate(ks):
+                    rows.append((ci, l, k, lo + b, lo + e))
+        else:
+            for l, (b, e) in enumerate(oracle.block_loop_ranges(hi - lo, chunk)):
+                rows.append((ci, l, -1, lo + b, lo + e))
+    return rows
+
+
+@pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
+def test_plan_matches_oracle_partition(L, coll):
+    cases = itertools.product((1, 2, 3, 8, 16), (0, 1, 7, 100, 4097, 1 << 16, 3_000_001), (1, 2, 5, 16),
+                              (16, 4096, 524_288), ("float32", "bfloat16", "int64"))
+    for n, count, c, cb, dt in cases:
+        if count // max(1, cb // 16) > 20_000:  # keep the Python side quick
+            continue
+        assert rs.debug_plan(coll, count, n, c, cb, dt) == _oracle_rows(coll, count, n, c, cb, dt), \
+            (coll, n, count, c, cb, dt)
+
+
+def test_plan_workload_shapes(L):
+    # 8 ranks, 64 MiB fp32, 8 channels, 512 KiB chunks: 2 full loops per channel
+    rows = rs.debug_plan("allreduce", 16_777_216, 8, 8, 524_288, "float32")
+    assert len(rows) == 8 * 2 * 8
+    assert all(e - b == 131_072 for (_, _, _, b, e) in rows)
+    # 8 ranks, 25 MiB bf16, 16 channels: one short loop, chunk 102,400
+    rows = rs.debug_plan("allreduce", 13_107_200, 8, 16, 524_288, "bfloat16")
+    assert len(rows) == 16 * 8
+    assert all(e - b == 102_400 for (_, _, _, b, e) in rows)
+
+
+def test_invalid_arguments_fail_before_touching_a_device(L):
+    h = ctypes.c_void_p(12345)
+    for nr, nc, p in ((0, 1, 0), (65, 1, 0), (4, 0, 0), (4, 65, 0), (4, 1, 3), (4, 1, -1)):
+        assert L.ringsim_comm_init(ctypes.byref(h), nr, nc, p) == 4
+        assert h.value == 12345  # untouched on error
+    assert L.ringsim_comm_init(None, 4, 1, 0) == 4
+    cfg = rs.Config()
+    cfg.chunk_bytes = 24  # not a multiple of 16
+    assert L.ringsim_comm_init_config(ctypes.byref(h), 4, 1, 0, ctypes.byref(cfg)) == 4
+    cfg = rs.Config()
+    cfg.slot_bytes = 1000
+    assert L.ringsim_comm_init_config(ctypes.byref(h), 4, 1, 0, ctypes.byref(cfg)) == 4
+    n = ctypes.c_size_t()
+    assert L.ringsim_debug_plan(0, 10, 4, 1, 24, 2, None, 0, ctypes.byref(n)) == 4
+    assert L.ringsim_debug_plan(0, 10, 4, 1, 16, 9, None, 0, ctypes.byref(n)) == 4
+    assert L.ringsim_debug_plan(7, 10, 4, 1, 16, 2, None, 0, ctypes.byref(n)) == 4
+
+
+def test_bad_handles_are_invalid_usage(L):
+    bogus = ctypes.c_void_p(0xdeadbeef)
+    arr = (ctypes.c_void_p * 4)()
+    assert L.ringsim_comm_destroy(None) == 5
+    assert L.ringsim_comm_destroy(bogus) == 5
+    assert L.ringsim_allreduce(bogus, arr, arr, 16, 2, 0, None) == 5
+    assert L.ringsim_reduce_scatter(bogus, arr, arr, 16, 2, 0, None) == 5
+    assert L.ringsim_all_gather(bogus, arr, arr, 16, 2, None) == 5
+    assert L.ringsim_alltoall(bogus, arr, arr, 16, 2, None) == 5
+    assert L.ringsim_abort(bogus) == 5
+    err = ctypes.c_int()
+    assert L.ringsim_get_async_error(bogus, ctypes.byref(err)) == 5
+    info = rs.CommInfo()
+    assert L.ringsim_comm_query(bogus, ctypes.byref(info)) == 5
+
+
+def test_config_defaults(L):
+    cfg = rs.config_default()
+    assert cfg.chunk_bytes == 524_288
+    assert cfg.nslots == 8
+    assert cfg.slot_bytes == 32_768
+    assert cfg.flag_threshold_bytes == 65_536

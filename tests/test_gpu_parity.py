@@ -1,0 +1,223 @@
+"""Parity of the HIP ring collectives with the CPU oracle (MI355X only).
+
+Every case runs the library through its C ABI on seeded synthetic inputs and
+compares the device result element by element with the oracle's replay of
+the same ring order: bit-exact for every dtype (the oracle rounds each hop
+exactly as the ring does), plus the fp64 error bounds for floating point.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import ring_all_reduce_allreduce_amd as rs
+import synth
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    rs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(n, count, dtype, seed, kind="normal"):
+    rng = np.random.default_rng(seed)
+    if dtype in ("int32", "int64"):
+        info = np.iinfo(np.int32 if dtype == "int32" else np.int64)
+        lo, hi = (-(1 << 20), 1 << 20) if kind == "normal" else (info.min, info.max)
+        return [rng.integers(lo, hi, count, endpoint=True).astype(oracle.STORAGE[dtype]) for _ in range(n)]
+    f = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+    if dtype == "bfloat16":
+        return [synth.f32_to_bf16_bits(x) for x in f]
+    return f
+
+
+def _run_allreduce(xs, dtype, op, nchannels, proto, chunk_bytes=None, inplace=False, **cfg):
+    n = len(xs)
+    count = xs[0].shape[0]
+    G.say(f"allreduce N={n} count={count} dtype={dtype} op={op} C={nchannels} proto={proto} "
+          f"chunk={chunk_bytes} inplace={inplace} cfg={cfg}")
+    comm = rs.comm_init(n, nchannels, proto, chunk_bytes=chunk_bytes, **cfg)
+    try:
+        send = [G.to_device(x, dtype) for x in xs]
+        recv = send if inplace else [G.empty_like_rank(count, dtype) for _ in range(n)]
+        rs.allreduce(comm, send, recv, op=op)
+        G.sync()
+        G.check_comm_ok(comm)
+        return [G.to_host(t, dtype) for t in recv]
+    finally:
+        rs.comm_destroy(comm)
+
+
+def _assert_same(got, want, dtype, what):
+    for r, (g, w) in enumerate(zip(got, want)):
+        mm = G.first_mismatch(g, w, dtype)
+        assert mm is None, f"{what}: rank {r} first mismatch at {mm}"
+
+
+def test_workload1_exact():
+    xs = synth.workload_inputs(1)
+    got = _run_allreduce(xs, "float32", "sum", 1, "bulk")
+    want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=1)
+    _assert_same(got, want, "float32", "workload 1")
+    exact = np.sum(np.stack(xs).astype(np.int64), axis=0).astype(np.float32)
+    assert np.array_equal(got[0], exact)
+
+
+@pytest.mark.parametrize("proto", ["bulk", "flag"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32", "int64"])
+def test_allreduce_matrix(proto, dtype):
+    seed = 100
+    for n in (2, 3, 8):
+        for count, nch, chunk in ((1, 1, 4096), (1000, 3, 4096), (100_003, 3, 4096), (70_001, 2, 524_288)):
+            ops = ("sum", "max") if n != 3 else ("sum", "min", "prod")
+            for op in ops:
+                seed += 1
+                xs = _inputs(n, count, dtype, seed)
+                got = _run_allreduce(xs, dtype, op, nch, proto, chunk_bytes=chunk)
+                want = oracle.ring_allreduce(xs, op, dtype, nchannels=nch,
+                                             chunk_bytes=min(chunk, 65536) if proto == "flag" else chunk)
+                _assert_same(got, want, dtype, f"N={n} count={count} C={nch} op={op}")
+
+
+@pytest.mark.parametrize("proto", ["bulk", "flag"])
+def test_allreduce_inplace_and_unaligned(proto):
+    import torch
+
+    n, count, dtype = 4, 50_001, "float32"
+    xs = _inputs(n, count, dtype, 7)
+    want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=2, chunk_bytes=8192)
+    got = _run_allreduce(xs, dtype, "sum", 2, proto, chunk_bytes=8192, inplace=True)
+    _assert_same(got, want, dtype, "in place")
+    # buffers offset by one element: element-wise path
+    G.say(f"allreduce unaligned proto={proto}")
+    comm = rs.comm_init(n, 2, proto, chunk_bytes=8192)
+    try:
+        base_s = [torch.zeros(count + 1, dtype=torch.float32, device="cuda:0") for _ in range(n)]
+        base_r = [torch.zeros(count + 1, dtype=torch.float32, device="cuda:0") for _ in range(n)]
+        for b, x in zip(base_s, xs):
+            b[1:].copy_(torch.from_numpy(x))
+        rs.allreduce(comm, [b[1:] for b in base_s], [b[1:] for b in base_r])
+        G.sync()
+        G.check_comm_ok(comm)
+        _assert_same([b[1:].cpu().numpy() for b in base_r], want, dtype, "unaligned")
+    finally:
+        rs.comm_destroy(comm)
+
+
+@pytest.mark.parametrize("proto", ["bulk", "flag"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int64"])
+def test_reduce_scatter(proto, dtype):
+    for n, rc, nch in ((2, 5000, 1), (5, 33_333, 3), (8, 65_536, 4)):
+        xs = _inputs(n, n * rc, dtype, 300 + n)
+        G.say(f"reduce_scatter N={n} recvcount={rc} dtype={dtype} C={nch} proto={proto}")
+        comm = rs.comm_init(n, nch, proto, chunk_bytes=16384)
+        try:
+            send = [G.to_device(x, dtype) for x in xs]
+            recv = [G.empty_like_rank(rc, dtype) for _ in range(n)]
+            rs.reduce_scatter(comm, send, recv, op="sum")
+            G.sync()
+            G.check_comm_ok(comm)
+            got = [G.to_host(t, dtype) for t in recv]
+        finally:
+            rs.comm_destroy(comm)
+        want = oracle.ring_reduce_scatter(xs, "sum", dtype, nchannels=nch, chunk_bytes=16384)
+        _assert_same(got, want, dtype, f"reduce_scatter N={n}")
+
+
+@pytest.mark.parametrize("proto", ["bulk", "flag"])
+def test_all_gather(proto):
+    for n, sc, nch, dtype in ((2, 777, 1, "bfloat16"), (6, 40_000, 3, "int32"), (8, 131_072, 8, "float32")):
+        xs = _inputs(n, sc, dtype, 400 + n)
+        G.say(f"all_gather N={n} sendcount={sc} dtype={dtype} C={nch} proto={proto}")
+        comm = rs.comm_init(n, nch, proto, chunk_bytes=32768)
+        try:
+            send = [G.to_device(x, dtype) for x in xs]
+            recv = [G.empty_like_rank(n * sc, dtype) for _ in range(n)]
+            rs.all_gather(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            got = [G.to_host(t, dtype) for t in recv]
+        finally:
+            rs.comm_destroy(comm)
+        want = oracle.ring_all_gather(xs, dtype, nchannels=nch, chunk_bytes=32768)
+        _assert_same(got, want, dtype, f"all_gather N={n}")
+
+
+def test_alltoall():
+    for n, cnt, dtype in ((1, 100, "float32"), (3, 1001, "bfloat16"), (8, 65_536, "bfloat16"), (4, 3, "int64")):
+        xs = _inputs(n, n * cnt, dtype, 500 + n)
+        G.say(f"alltoall N={n} count={cnt} dtype={dtype}")
+        comm = rs.comm_init(n, 1, "auto")
+        try:
+            send = [G.to_device(x, dtype) for x in xs]
+            recv = [G.empty_like_rank(n * cnt, dtype) for _ in range(n)]
+            rs.alltoall(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            got = [G.to_host(t, dtype) for t in recv]
+        finally:
+            rs.comm_destroy(comm)
+        _assert_same(got, oracle.alltoall(xs, dtype), dtype, f"alltoall N={n}")
+
+
+def test_degenerate_shapes():
+    # one rank: local copy; zero count: no-op; 16 ranks x 2 elements: most chunks empty
+    for n, count, nch, proto in ((1, 1000, 1, "bulk"), (16, 2, 16, "bulk"), (16, 2, 16, "flag"),
+                                 (16, 5, 1, "bulk"), (7, 13, 4, "flag")):
+        xs = _inputs(n, count, "int32", 600 + n + count)
+        got = _run_allreduce(xs, "int32", "sum", nch, proto)
+        want = oracle.ring_allreduce(xs, "sum", "int32", nchannels=nch)
+        _assert_same(got, want, "int32", f"degenerate N={n} count={count}")
+    comm = rs.comm_init(4, 2, "auto")
+    try:
+        import torch
+
+        t = [torch.zeros(0, device="cuda:0") for _ in range(4)]
+        rs.allreduce(comm, t, t, count=0)
+        G.sync()
+        G.check_comm_ok(comm)
+    finally:
+        rs.comm_destroy(comm)
+
+
+def test_back_to_back_calls_one_stream():
+    # many collectives of different shapes and both protocols on one stream:
+    # the FIFO counters carry over from call to call
+    n, dtype = 8, "float32"
+    comm = rs.comm_init(n, 4, "auto", chunk_bytes=16384)
+    try:
+        cases = []
+        for k in range(24):
+            count = [10, 3000, 20_000, 250_000][k % 4] + k
+            xs = _inputs(n, count, dtype, 700 + k)
+            send = [G.to_device(x, dtype) for x in xs]
+            recv = [G.empty_like_rank(count, dtype) for _ in range(n)]
+            G.say(f"back-to-back call {k} count={count}")
+            rs.allreduce(comm, send, recv)
+            cases.append((xs, recv, count))
+        G.sync()
+        G.check_comm_ok(comm)
+        for xs, recv, count in cases:
+            proto_chunk = 16384
+            want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=4, chunk_bytes=proto_chunk)
+            _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"back-to-back count={count}")
+    finally:
+        rs.comm_destroy(comm)
+
+
+def test_workload2_full_size():
+    w = synth.WORKLOADS[2]
+    xs = synth.workload_inputs(2)
+    got = _run_allreduce(xs, "float32", "sum", w["nchannels"], "bulk", chunk_bytes=w["chunk_bytes"])
+    want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=w["nchannels"], chunk_bytes=w["chunk_bytes"])
+    _assert_same(got, want, "float32", "workload 2")
+    st = np.stack(xs).astype(np.float64)
+    err = np.abs(got[3].astype(np.float64) - st.sum(axis=0))
+    assert np.all(err <= 1e-6 * np.abs(st).sum(axis=0))
