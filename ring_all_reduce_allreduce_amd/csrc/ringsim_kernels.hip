@@ -13,9 +13,10 @@
 //
 // Two protocols:
 //   bulk  FIFO slots hold raw payload; readiness travels in separate 64-bit
-//         step counters (tail: slots filled, head: slots drained), published
-//         with agent-scope release after the slot's stores complete and read
-//         with agent-scope acquire before the slot is read (Simple).
+//         step counters (tail: slots filled, head: slots drained). Slot data
+//         is written and read with device-scope coherent (SC1) accesses, so a
+//         counter published once those accesses have completed is enough to
+//         order them; no L2 writeback or invalidate is needed (Simple).
 //   flag  FIFO lines of 16 bytes carry two {4-byte payload, 4-byte flag}
 //         words; each 8-byte word is written and read as one 64-bit access,
 //         so a receiver that sees the expected flag also sees its payload.
@@ -163,8 +164,6 @@ __device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
 __device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 // Wait until every global load and store this thread issued has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -232,75 +231,118 @@ __device__ __forceinline__ uint64_t wait_geq(const uint64_t* p, uint64_t target,
 // Bulk data movement: one FIFO slot worth of a unit
 // ---------------------------------------------------------------------------
 
-// Whole 16-byte vectors: x = RED ? op(src, loc) : src, then x -> fout and/or
-// uout. Full tiles run unguarded so that all loads of a tile are in flight
-// before the first use; the last partial tile is guarded.
-template <int DT, int OP, bool RED, bool FOUT, bool UOUT>
-__device__ __forceinline__ void move_vec(int64_t nv, const u32x4* __restrict__ src, const u32x4* __restrict__ l4,
-                                         u32x4* __restrict__ f4, u32x4* __restrict__ u4) {
+// FIFO slots are accessed through buffer resources (bounds-checked against the
+// slot size) with device-scope coherence (SC1): a store is visible to every
+// XCD once it completes and a load never returns a stale line, so a step
+// counter published after the stores complete is all the consumer needs - no
+// L2 writeback or invalidate on the data path. User buffers use plain global
+// accesses marked non-temporal (each byte is touched once per launch).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit raw data, no swizzle
+constexpr int kPolFifo = 16;            // SC1: device scope
+constexpr int kPolFifoStream = 16 | 2;  // SC1 + NT: device scope, no reuse expected
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+template <typename T>
+__device__ __forceinline__ T fifo_ld(rsrc_t r, int off) {
+  if constexpr (sizeof(T) == 2) return (T)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kPolFifoStream);
+  else if constexpr (sizeof(T) == 4) return (T)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kPolFifoStream);
+  else return (T)__builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolFifoStream));
+}
+
+template <typename T>
+__device__ __forceinline__ void fifo_st(T v, rsrc_t r, int off) {
+  if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, kPolFifo);
+  else if constexpr (sizeof(T) == 4) __builtin_amdgcn_raw_buffer_store_b32((unsigned int)v, r, off, 0, kPolFifo);
+  else __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, (uint64_t)v), r, off, 0, kPolFifo);
+}
+
+__device__ __forceinline__ u32x4 fifo_ld4(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolFifoStream));
+}
+__device__ __forceinline__ void fifo_st4(u32x4 v, rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolFifo);
+}
+
+// Whole 16-byte vectors: x = src (FIFO when SRC_FIFO, else user data loc),
+// x = op(x, loc) when RED, then x -> FIFO fout and/or user uout. Full tiles run
+// unguarded so that every load of a tile is in flight before the first use.
+template <int DT, int OP, bool SRC_FIFO, bool RED, bool FOUT, bool UOUT>
+__device__ __forceinline__ void move_vec(int64_t nv, rsrc_t fin, const u32x4* __restrict__ loc, rsrc_t fout,
+                                         u32x4* __restrict__ uout) {
   const int tid = threadIdx.x;
-  constexpr int64_t kTile = (int64_t)kThreads * kUnroll;
-  int64_t base = 0;
-  for (; base + kTile <= nv; base += kTile) {
+  constexpr int kTile = kThreads * kUnroll;
+  auto load_src = [&](int i) -> u32x4 {
+    if constexpr (SRC_FIFO) return fifo_ld4(fin, i * 16);
+    else return __builtin_nontemporal_load(loc + i);
+  };
+  auto store = [&](int i, u32x4 v) {
+    if constexpr (FOUT) fifo_st4(v, fout, i * 16);
+    if constexpr (UOUT) __builtin_nontemporal_store(v, uout + i);
+  };
+  int base = 0;
+  const int n = (int)nv;
+  for (; base + kTile <= n; base += kTile) {
     u32x4 v[kUnroll];
     u32x4 x[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[base + u * kThreads + tid];
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_src(base + u * kThreads + tid);
     if constexpr (RED) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) x[u] = l4[base + u * kThreads + tid];
+      for (int u = 0; u < kUnroll; ++u) x[u] = __builtin_nontemporal_load(loc + base + u * kThreads + tid);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) v[u] = VOp<DT, OP>::v4(v[u], x[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if constexpr (FOUT) f4[base + u * kThreads + tid] = v[u];
-      if constexpr (UOUT) u4[base + u * kThreads + tid] = v[u];
-    }
+    for (int u = 0; u < kUnroll; ++u) store(base + u * kThreads + tid, v[u]);
   }
-  for (int64_t i = base + tid; i < nv; i += kThreads) {
-    u32x4 v = src[i];
-    if constexpr (RED) v = VOp<DT, OP>::v4(v, l4[i]);
-    if constexpr (FOUT) f4[i] = v;
-    if constexpr (UOUT) u4[i] = v;
+  for (int i = base + tid; i < n; i += kThreads) {
+    u32x4 v = load_src(i);
+    if constexpr (RED) v = VOp<DT, OP>::v4(v, __builtin_nontemporal_load(loc + i));
+    store(i, v);
   }
 }
 
-// One FIFO slot worth of a unit: x = fin ? (loc ? op(fin, loc) : fin) : loc,
-// then x -> fout and/or uout. fin/fout are FIFO slots (16-byte aligned);
-// loc/uout are user data, vector-moved only when vec_ok.
+// One FIFO slot worth of a unit (n elements): x = fin ? (loc ? op(fin, loc)
+// : fin) : loc, then x -> fout and/or uout. fin/fout are FIFO slots of
+// slot_bytes; loc/uout are user data, vector-moved only when vec_ok.
 template <int DT, int OP>
 __device__ __forceinline__ void move_slice(int64_t n, const char* fin, const char* loc, char* fout, char* uout,
-                                           int vec_ok) {
+                                           int slot_bytes, int vec_ok) {
   using T = typename Elem<DT>::T;
   constexpr int A = 16 / (int)sizeof(T);
   const int64_t nv = vec_ok ? n / A : 0;
+  const rsrc_t rin = make_rsrc(fin, fin ? slot_bytes : 0);
+  const rsrc_t rout = make_rsrc(fout, fout ? slot_bytes : 0);
+  const u32x4* l4 = reinterpret_cast<const u32x4*>(loc);
+  u32x4* u4 = reinterpret_cast<u32x4*>(uout);
   if (nv > 0) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(fin ? fin : loc);
-    const u32x4* l4 = reinterpret_cast<const u32x4*>(loc);
-    u32x4* f4 = reinterpret_cast<u32x4*>(fout);
-    u32x4* u4 = reinterpret_cast<u32x4*>(uout);
     if (fin && loc) {
-      if (fout && uout) move_vec<DT, OP, true, true, true>(nv, src, l4, f4, u4);
-      else if (fout) move_vec<DT, OP, true, true, false>(nv, src, l4, f4, u4);
-      else move_vec<DT, OP, true, false, true>(nv, src, l4, f4, u4);
+      if (fout && uout) move_vec<DT, OP, true, true, true, true>(nv, rin, l4, rout, u4);
+      else if (fout) move_vec<DT, OP, true, true, true, false>(nv, rin, l4, rout, u4);
+      else move_vec<DT, OP, true, true, false, true>(nv, rin, l4, rout, u4);
+    } else if (fin) {
+      if (fout && uout) move_vec<DT, OP, true, false, true, true>(nv, rin, l4, rout, u4);
+      else if (fout) move_vec<DT, OP, true, false, true, false>(nv, rin, l4, rout, u4);
+      else move_vec<DT, OP, true, false, false, true>(nv, rin, l4, rout, u4);
     } else {
-      if (fout && uout) move_vec<DT, OP, false, true, true>(nv, src, l4, f4, u4);
-      else if (fout) move_vec<DT, OP, false, true, false>(nv, src, l4, f4, u4);
-      else move_vec<DT, OP, false, false, true>(nv, src, l4, f4, u4);
+      if (fout && uout) move_vec<DT, OP, false, false, true, true>(nv, rin, l4, rout, u4);
+      else move_vec<DT, OP, false, false, true, false>(nv, rin, l4, rout, u4);
     }
   }
   // Elements past the last whole vector (or all of them when user buffers
   // are not 16-byte aligned).
-  const T* s1 = reinterpret_cast<const T*>(fin ? fin : loc);
-  const T* l1 = (fin && loc) ? reinterpret_cast<const T*>(loc) : nullptr;
-  T* f1 = reinterpret_cast<T*>(fout);
+  const T* l1 = reinterpret_cast<const T*>(loc);
   T* o1 = reinterpret_cast<T*>(uout);
   for (int64_t i = nv * A + threadIdx.x; i < n; i += kThreads) {
-    T x = s1[i];
-    if (l1) x = VOp<DT, OP>::one(x, l1[i]);
-    if (f1) f1[i] = x;
-    if (o1) o1[i] = x;
+    const int off = (int)(i * (int64_t)sizeof(T));
+    T x = fin ? fifo_ld<T>(rin, off) : l1[i];
+    if (fin && loc) x = VOp<DT, OP>::one(x, l1[i]);
+    if (fout) fifo_st<T>(x, rout, off);
+    if (uout) o1[i] = x;
   }
 }
 
@@ -418,33 +460,29 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
     for (int64_t s = 0; s < m; s += slice) {
       const int64_t ns = min64(slice, m - s);
       if (threadIdx.x == 0 && !stop) {
-        // A value already seen (and acquired) may cover this step; otherwise
-        // poll, then acquire so that the producer's slot stores (or the
-        // consumer's drained-slot loads) are ordered before what follows.
-        bool fresh = false;
+        // A counter value seen earlier may already cover this step. The
+        // barrier below keeps every thread's slot accesses after the wait.
         const uint64_t need_tail = in_base + nrecv + 1;
         if (recv && known_tail < need_tail) {
           known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
           stop = known_tail == 0;
-          fresh = true;
         }
         const uint64_t need_head = out_base + nsent + 1 - nslots;
         if (!stop && send && nsent + 1 > nslots && known_head < need_head) {
           known_head = wait_geq(&p.out_ctr->head, need_head, wc);
           stop = known_head == 0;
-          fresh = true;
         }
-        if (fresh) fence_acquire();
       }
       __syncthreads();
       const char* fin = recv ? p.in_fifo + ((in_base + nrecv) % nslots) * a.slot_bytes : nullptr;
       char* fout = send ? p.out_fifo + ((out_base + nsent) % nslots) * a.slot_bytes : nullptr;
       move_slice<DT, OP>(ns, fin, use_local ? local + s * E : nullptr, fout, store ? out + s * E : nullptr,
-                         a.vec_ok);
+                         a.slot_bytes, a.vec_ok);
+      // Every thread's FIFO stores (device-coherent) and FIFO loads have
+      // completed before thread 0 publishes the new tail and head.
       wait_vmem();
       __syncthreads();
       if (threadIdx.x == 0) {
-        fence_release();
         if (send) st_relaxed(&p.out_ctr->tail, out_base + nsent + 1);
         if (recv) st_relaxed(&p.in_ctr->head, in_base + nrecv + 1);
       }
