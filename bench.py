@@ -99,14 +99,18 @@ def bus_factor(coll: str, n: int) -> float:
 def load_traffic(name: str, src_hash: str):
     """Counter-measured HBM bytes per launch, if a summary for this workload
     and this exact kernel source is committed under profiles/."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(p):
         return None
+    t = {}
     with open(p) as f:
-        t = json.load(f)
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                t[k.strip()] = v.strip()
     if t.get("kernel_source_hash") != src_hash:
         return None
-    return t.get("bytes_per_launch")
+    return int(t["bytes_per_launch"])
 
 
 def make_inputs(w: dict):
@@ -184,6 +188,35 @@ def d2d_copy_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2 * nbytes / t / 1e9
 
 
+def copy_calibration(args) -> int:
+    """Known-size reference for the byte counters: the copy kernel moving
+    1 GiB (reads 1 GiB, writes 1 GiB) per launch."""
+    import torch
+
+    import ring_all_reduce_allreduce_amd as rs
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    comm = rs.comm_init(1, 1, "bulk")
+    for _ in range(args.warmup):
+        rs.alltoall(comm, [src], [dst])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        rs.alltoall(comm, [src], [dst])
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / args.steps
+    ok = bool(torch.equal(src, dst))
+    rs.comm_destroy(comm)
+    print(json.dumps({"metric": "copy kernel HBM bandwidth (read+write)", "value": round(2 * nbytes / t / 1e9, 1),
+                      "unit": "GB/s", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                      "launch_avg_us": round(t * 1e6, 2), "copy_ok": ok}), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +228,9 @@ def main() -> int:
     ap.add_argument("--wpc", type=int, default=0, help="workgroups per channel (0 = library default)")
     ap.add_argument("--slot-bytes", type=int, default=0)
     ap.add_argument("--nslots", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time the library's copy kernel on 1 GiB (a one-rank all-to-all) instead; used to "
+                         "scale the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +242,9 @@ def main() -> int:
     import torch
 
     import ring_all_reduce_allreduce_amd as rs
+
+    if args.copy_calibration:
+        return copy_calibration(args)
 
     w = WORKLOADS[args.workload]
     n, dtype, coll = w["nranks"], w["dtype"], w["coll"]
