@@ -135,7 +135,12 @@ typedef struct {
   uint64_t calls;              /* collective calls enqueued so far */
 } ringsim_comm_info_t;
 
-/* Fills *cfg with the defaults (environment overrides included). */
+/* Fills *cfg with the defaults. Environment overrides, read by this call:
+ * RINGSIM_CHUNK_BYTES, RINGSIM_WPC, RINGSIM_SLOT_BYTES, RINGSIM_NSLOTS,
+ * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD; RINGSIM_DEBUG=WARN|INFO logs to
+ * stderr. Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
+ * the workgroups of simulated rank r return at once, so that the bounded
+ * waits of its neighbours expire and the failure path can be exercised. */
 ringsim_result_t ringsim_config_default(ringsim_config_t* cfg);
 
 /* Creates a communicator of `nranks` (1..RINGSIM_MAX_RANKS) simulated ranks

@@ -74,6 +74,7 @@ struct ringsim_comm {
   size_t slot_bytes;
   size_t flag_threshold;
   int timeout_ms;
+  int skip_rank;  // testing knob (RINGSIM_DEBUG_SKIP_RANK), -1 = off
   uint64_t timeout_ticks;
   int compute_units;
   int blocks_per_cu;
@@ -163,6 +164,7 @@ void fill_common(const ringsim_comm* c, RingArgs* a, const void* const* sb, void
   a->host_abort = c->host_words_dev;
   a->host_err = c->host_words_dev + 1;
   a->timeout_ticks = c->timeout_ticks;
+  a->skip_rank = c->skip_rank;
 }
 
 // Picks the protocol and fills the protocol-dependent launch geometry.
@@ -342,6 +344,9 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->slot_bytes = cfg.slot_bytes;
   c->flag_threshold = cfg.flag_threshold_bytes;
   c->timeout_ms = cfg.timeout_ms;
+  // Testing knob: the workgroups of this rank return without doing anything,
+  // so that its neighbours' bounded waits expire (failure-path tests).
+  c->skip_rank = (int)env_long("RINGSIM_DEBUG_SKIP_RANK", -1);
   c->timeout_ticks = (uint64_t)cfg.timeout_ms * (uint64_t)clock_khz;
   c->compute_units = cus;
   c->blocks_per_cu = per_cu;

@@ -58,6 +58,7 @@ struct RingArgs {
   const uint32_t* host_abort;  // host-mapped word set by ringsim_abort
   uint32_t* host_err;   // host-mapped error word
   uint64_t timeout_ticks;  // bound on one wait, in wall-clock ticks
+  int skip_rank;        // testing knob: workgroups of this rank return at once (-1 = none)
 };
 
 struct CopyArgs {

@@ -439,6 +439,7 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int64_t E = sizeof(T);
   const Pipe p = locate(a);
+  if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
   __shared__ uint64_t s_base[2];
   if (threadIdx.x == 0) {
     // Each side's own counter tells where the previous call left this FIFO.
@@ -555,6 +556,7 @@ __global__ void __launch_bounds__(kThreads) ring_flag_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int64_t E = sizeof(T);
   const Pipe p = locate(a);
+  if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
   __shared__ uint64_t s_base[2];
   __shared__ uint64_t s_head;
   if (threadIdx.x == 0) {

@@ -121,3 +121,40 @@ def a2a_inputs(nranks: int = 8, tokens: int = 512, hidden: int = 4096, dtype: st
     """All-to-all buffers: each rank holds ``nranks`` chunks of tokens x hidden."""
     n = nranks * tokens * hidden
     return rank_inputs(workload, nranks, n, dtype, "uniform", 1.0, bucket=bucket)
+
+
+# Device-side generators for the full-size workloads --------------------------
+# Host generation of gigabytes of draws takes minutes; these use torch's seeded
+# device RNG instead (same seed formula). Tests copy the sampled elements they
+# check back to the host and give those to the oracle.
+
+def device_inputs(workload: int, nranks: int, n: int, dtype: str, dist: str, scale: float = 1.0,
+                  lo: int = 0, hi: int = 0, bucket: int = 0, device: str = "cuda:0"):
+    """One seeded device buffer of ``n`` elements per rank (torch tensors)."""
+    import torch
+
+    tdt = {"int32": torch.int32, "int64": torch.int64, "float32": torch.float32,
+           "bfloat16": torch.bfloat16}[dtype]
+    out = []
+    for r in range(nranks):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed_for(workload, r, bucket))
+        if dist == "int":
+            t = torch.randint(lo, hi + 1, (n,), generator=g, device=device, dtype=torch.int64)
+            out.append(t.to(tdt))
+        elif dist == "normal":
+            t = torch.randn(n, generator=g, device=device, dtype=torch.float32) * scale
+            out.append(t.to(tdt))
+        elif dist == "uniform":
+            t = (torch.rand(n, generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0) * scale
+            out.append(t.to(tdt))
+        else:
+            raise ValueError(dist)
+    return out
+
+
+def ddp_bucket_ranks(bucket: int, nranks: int = 8, distinct: int = 5) -> tuple[int, list[int]]:
+    """The 40 DDP buckets reuse ``distinct`` seeded base buckets: bucket b takes
+    base bucket b mod distinct, and rank r holds that base bucket's rank
+    (r + b // distinct) mod nranks. Returns (base bucket, source rank per rank)."""
+    return bucket % distinct, [(r + bucket // distinct) % nranks for r in range(nranks)]

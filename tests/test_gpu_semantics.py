@@ -1,0 +1,165 @@
+"""Call semantics on the MI355X: calls return before the device finishes and
+keep stream order; failures are forced from the host (a rank whose
+workgroups never take part, a short wait bound, or an abort request) and
+every kernel still drains on its own."""
+import os
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import ring_all_reduce_allreduce_amd as rs
+import synth
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    rs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sleep_cycles_for(ms):
+    """torch.cuda._sleep takes device clock cycles; calibrate against events."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cycles = 10_000_000
+    e0.record()
+    torch.cuda._sleep(cycles)
+    e1.record()
+    torch.cuda.synchronize()
+    per_ms = cycles / max(e0.elapsed_time(e1), 1e-3)
+    return int(per_ms * ms)
+
+
+def test_call_returns_before_completion_and_keeps_stream_order():
+    """A 16 MiB all-reduce enqueued behind a ~50 ms device sleep returns to the
+    host at once, reports IN_PROGRESS, and is correct after the stream syncs
+    (the call behaves like ncclAllReduce under ProcessGroupNCCL)."""
+    import torch
+
+    n, count = 4, 4 << 20
+    xs = synth.rank_inputs(2, n, count, "float32", "normal", bucket=9)
+    send = [G.to_device(x, "float32") for x in xs]
+    recv = [torch.empty_like(s) for s in send]
+    comm = rs.comm_init(n, 4, "auto")
+    try:
+        rs.allreduce(comm, send, recv)  # warm up kernels and code paths
+        G.sync()
+        cycles = _sleep_cycles_for(50)
+        G.say(f"sleep {cycles} cycles then allreduce")
+        torch.cuda._sleep(cycles)
+        t0 = time.perf_counter()
+        rs.allreduce(comm, send, recv)
+        t_call = time.perf_counter() - t0
+        state = rs.get_async_error(comm)
+        t1 = time.perf_counter()
+        G.sync()
+        t_sync = time.perf_counter() - t1
+        assert t_call < 0.010, t_call
+        assert state == 7, state  # IN_PROGRESS
+        assert t_sync > 0.020, t_sync
+        assert rs.get_async_error(comm) == rs.SUCCESS
+        want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=4)
+        for r in range(n):
+            assert G.bits_equal(G.to_host(recv[r], "float32"), want[r], "float32")
+    finally:
+        rs.comm_destroy(comm)
+
+
+@pytest.mark.parametrize("proto", ["bulk", "flag"])
+def test_missing_rank_times_out_and_poisons_the_comm(proto, monkeypatch):
+    import torch
+
+    monkeypatch.setenv("RINGSIM_DEBUG_SKIP_RANK", "2")
+    n, count = 4, 200_000 if proto == "bulk" else 1000
+    comm = rs.comm_init(n, 2, proto, timeout_ms=50)
+    monkeypatch.delenv("RINGSIM_DEBUG_SKIP_RANK")
+    try:
+        send = [torch.ones(count, device="cuda:0") for _ in range(n)]
+        recv = [torch.zeros(count, device="cuda:0") for _ in range(n)]
+        G.say(f"skip rank 2, timeout 50 ms, proto {proto}")
+        t0 = time.perf_counter()
+        rs.allreduce(comm, send, recv)
+        G.sync()
+        dt = time.perf_counter() - t0
+        assert dt < 5.0, dt
+        assert rs.get_async_error(comm) == 3  # INTERNAL_ERROR: a wait expired
+        with pytest.raises(rs.RingsimError) as ei:
+            rs.allreduce(comm, send, recv)
+        assert ei.value.code == 3
+    finally:
+        rs.comm_destroy(comm)
+
+
+def test_abort_stops_a_stalled_collective(monkeypatch):
+    import torch
+
+    monkeypatch.setenv("RINGSIM_DEBUG_SKIP_RANK", "1")
+    n, count = 4, 200_000
+    comm = rs.comm_init(n, 2, "bulk", timeout_ms=20_000)
+    monkeypatch.delenv("RINGSIM_DEBUG_SKIP_RANK")
+    try:
+        send = [torch.ones(count, device="cuda:0") for _ in range(n)]
+        recv = [torch.zeros(count, device="cuda:0") for _ in range(n)]
+        G.say("skip rank 1, timeout 20 s, abort after 100 ms")
+        rs.allreduce(comm, send, recv)
+        time.sleep(0.1)
+        assert rs.get_async_error(comm) == 7  # still spinning
+        t0 = time.perf_counter()
+        rs.abort(comm)
+        G.sync()
+        dt = time.perf_counter() - t0
+        assert dt < 2.0, dt  # far below the 20 s bound
+        assert rs.get_async_error(comm) == 8  # ABORTED
+        with pytest.raises(rs.RingsimError) as ei:
+            rs.allreduce(comm, send, recv)
+        assert ei.value.code == 8
+    finally:
+        rs.comm_destroy(comm)
+
+
+def test_comm_reuse_after_destroy_is_invalid_usage():
+    import ctypes
+
+    comm = rs.comm_init(2, 1, "auto")
+    h = comm.handle
+    rs.comm_destroy(comm)
+    arr = (ctypes.c_void_p * 2)()
+    assert rs.lib().ringsim_allreduce(ctypes.c_void_p(h), arr, arr, 4, 2, 0, None) == 5
+    assert rs.lib().ringsim_comm_destroy(ctypes.c_void_p(h)) == 5
+
+
+def test_bad_device_arguments():
+    import torch
+
+    comm = rs.comm_init(2, 1, "auto")
+    try:
+        t = [torch.zeros(64, device="cuda:0") for _ in range(2)]
+        with pytest.raises(rs.RingsimError) as ei:
+            rs.allreduce(comm, t, t, op=9)
+        assert ei.value.code == 4
+        with pytest.raises(rs.RingsimError) as ei:
+            rs.allreduce(comm, [0, t[1].data_ptr()], [t[0].data_ptr(), t[1].data_ptr()], count=64, dtype="float32")
+        assert ei.value.code == 4
+        with pytest.raises(rs.RingsimError) as ei:  # not element aligned
+            rs.allreduce(comm, [t[0].data_ptr() + 2, t[1].data_ptr()], [t[0].data_ptr(), t[1].data_ptr()],
+                         count=8, dtype="float32")
+        assert ei.value.code == 4
+        with pytest.raises(rs.RingsimError) as ei:  # all-to-all cannot run in place
+            rs.alltoall(comm, t, t)
+        assert ei.value.code == 4
+        G.sync()
+        assert rs.get_async_error(comm) == rs.SUCCESS
+        info = rs.comm_query(comm)
+        assert info["nranks"] == 2 and info["compute_units"] > 0
+    finally:
+        rs.comm_destroy(comm)
