@@ -305,10 +305,14 @@ def main() -> int:
         if not ok:
             return 1
 
-    # Timed region: K steps, per-launch HIP events on the launch stream.
+    # Timed region: K steps, per-launch HIP events on the launch stream. A
+    # short device sleep goes first so that every timed launch is already
+    # queued when the one before it ends: event intervals then hold device
+    # time only, not the host's launch latency.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    torch.cuda._sleep(2_000_000)
     t0 = time.perf_counter()
     for k in range(args.steps):
         starts[k].record(stream)

@@ -75,6 +75,7 @@ struct ringsim_comm {
   size_t flag_threshold;
   int timeout_ms;
   int skip_rank;  // testing knob (RINGSIM_DEBUG_SKIP_RANK), -1 = off
+  int lds_stage;  // bulk kernel stages each step's own operand in LDS
   uint64_t timeout_ticks;
   int compute_units;
   int blocks_per_cu;
@@ -188,6 +189,7 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, size_t bytes_per_rank, int e
     a->nslots = c->nslots;
     a->slot_bytes = (int)c->slot_bytes;
     a->chunk = (int64_t)c->chunk_bytes / esize;
+    a->lds_stage = c->lds_stage;
   }
 }
 
@@ -308,7 +310,10 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
       hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || cus <= 0 ||
       clock_khz <= 0)
     return RINGSIM_UNHANDLED_DEVICE_ERROR;
-  const int per_cu = ring_blocks_per_cu();
+  // Bulk steps stage their own operand in LDS (double-buffered) unless the
+  // slot is too large or RINGSIM_LDS_STAGE=0.
+  const int lds_stage = cfg.slot_bytes <= (size_t)kMaxStagedSlotBytes && env_long("RINGSIM_LDS_STAGE", 1) != 0;
+  const int per_cu = ring_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0);
   if (per_cu <= 0) return RINGSIM_UNHANDLED_DEVICE_ERROR;
   const int64_t max_resident = (int64_t)per_cu * cus;
 
@@ -347,6 +352,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Testing knob: the workgroups of this rank return without doing anything,
   // so that its neighbours' bounded waits expire (failure-path tests).
   c->skip_rank = (int)env_long("RINGSIM_DEBUG_SKIP_RANK", -1);
+  c->lds_stage = lds_stage;
   c->timeout_ticks = (uint64_t)cfg.timeout_ms * (uint64_t)clock_khz;
   c->compute_units = cus;
   c->blocks_per_cu = per_cu;
@@ -381,9 +387,9 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   }
   RS_LOG(kLogInfo,
          "comm %p: nranks %d nchannels %d proto %d wpc %d nslots %d slot %zu chunk %zu fifo %zu B flag fifo %zu B "
-         "resident %d/CU x %d CUs",
+         "lds stage %d resident %d/CU x %d CUs",
          (void*)c, nranks, nchannels, proto, wpc, nslots, cfg.slot_bytes, cfg.chunk_bytes, c->fifo_bytes,
-         c->flag_fifo_bytes, per_cu, cus);
+         c->flag_fifo_bytes, lds_stage, per_cu, cus);
   *comm = c;
   return RINGSIM_SUCCESS;
 }

@@ -59,6 +59,7 @@ struct RingArgs {
   uint32_t* host_err;   // host-mapped error word
   uint64_t timeout_ticks;  // bound on one wait, in wall-clock ticks
   int skip_rank;        // testing knob: workgroups of this rank return at once (-1 = none)
+  int lds_stage;        // bulk: stage each step's own operand in LDS (2 x slot_bytes dynamic LDS)
 };
 
 struct CopyArgs {
@@ -74,8 +75,12 @@ struct CopyArgs {
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_flag(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
-// Max co-resident workgroups per CU over every ring kernel instantiation.
-int ring_blocks_per_cu();
+// Max co-resident workgroups per CU over every ring kernel instantiation, the
+// bulk kernels launched with `bulk_lds_bytes` of dynamic LDS.
+int ring_blocks_per_cu(size_t bulk_lds_bytes);
+// Largest bulk slot that is staged in LDS (two buffers must fit beside a
+// second workgroup's on the 160 KiB of a CU).
+constexpr int kMaxStagedSlotBytes = 64 * 1024;
 
 inline int dtype_size(int dtype) {
   switch (dtype) {

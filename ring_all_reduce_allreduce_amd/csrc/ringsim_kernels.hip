@@ -270,14 +270,20 @@ __device__ __forceinline__ void fifo_st4(u32x4 v, rsrc_t r, int off) {
 // Whole 16-byte vectors: x = src (FIFO when SRC_FIFO, else user data loc),
 // x = op(x, loc) when RED, then x -> FIFO fout and/or user uout. Full tiles run
 // unguarded so that every load of a tile is in flight before the first use.
-template <int DT, int OP, bool SRC_FIFO, bool RED, bool FOUT, bool UOUT>
+template <int DT, int OP, bool SRC_FIFO, bool RED, bool FOUT, bool UOUT, bool LOC_LDS = false>
 __device__ __forceinline__ void move_vec(int64_t nv, rsrc_t fin, const u32x4* __restrict__ loc, rsrc_t fout,
                                          u32x4* __restrict__ uout) {
   const int tid = threadIdx.x;
   constexpr int kTile = kThreads * kUnroll;
+  // The rank's own operand: staged in LDS by the previous step, or streamed
+  // from HBM (read once: non-temporal).
+  auto load_loc = [&](int i) -> u32x4 {
+    if constexpr (LOC_LDS) return loc[i];
+    else return __builtin_nontemporal_load(loc + i);
+  };
   auto load_src = [&](int i) -> u32x4 {
     if constexpr (SRC_FIFO) return fifo_ld4(fin, i * 16);
-    else return __builtin_nontemporal_load(loc + i);
+    else return load_loc(i);
   };
   auto store = [&](int i, u32x4 v) {
     if constexpr (FOUT) fifo_st4(v, fout, i * 16);
@@ -292,7 +298,7 @@ __device__ __forceinline__ void move_vec(int64_t nv, rsrc_t fin, const u32x4* __
     for (int u = 0; u < kUnroll; ++u) v[u] = load_src(base + u * kThreads + tid);
     if constexpr (RED) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) x[u] = __builtin_nontemporal_load(loc + base + u * kThreads + tid);
+      for (int u = 0; u < kUnroll; ++u) x[u] = load_loc(base + u * kThreads + tid);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) v[u] = VOp<DT, OP>::v4(v[u], x[u]);
     }
@@ -301,7 +307,7 @@ __device__ __forceinline__ void move_vec(int64_t nv, rsrc_t fin, const u32x4* __
   }
   for (int i = base + tid; i < n; i += kThreads) {
     u32x4 v = load_src(i);
-    if constexpr (RED) v = VOp<DT, OP>::v4(v, __builtin_nontemporal_load(loc + i));
+    if constexpr (RED) v = VOp<DT, OP>::v4(v, load_loc(i));
     store(i, v);
   }
 }
@@ -309,9 +315,11 @@ __device__ __forceinline__ void move_vec(int64_t nv, rsrc_t fin, const u32x4* __
 // One FIFO slot worth of a unit (n elements): x = fin ? (loc ? op(fin, loc)
 // : fin) : loc, then x -> fout and/or uout. fin/fout are FIFO slots of
 // slot_bytes; loc/uout are user data, vector-moved only when vec_ok.
+// `staged` (LDS, may be null) holds the whole-vector part of `loc`, loaded by
+// the previous step; the rest of `loc` is read from memory.
 template <int DT, int OP>
 __device__ __forceinline__ void move_slice(int64_t n, const char* fin, const char* loc, char* fout, char* uout,
-                                           int slot_bytes, int vec_ok) {
+                                           int slot_bytes, int vec_ok, const u32x4* staged = nullptr) {
   using T = typename Elem<DT>::T;
   constexpr int A = 16 / (int)sizeof(T);
   const int64_t nv = vec_ok ? n / A : 0;
@@ -319,7 +327,16 @@ __device__ __forceinline__ void move_slice(int64_t n, const char* fin, const cha
   const rsrc_t rout = make_rsrc(fout, fout ? slot_bytes : 0);
   const u32x4* l4 = reinterpret_cast<const u32x4*>(loc);
   u32x4* u4 = reinterpret_cast<u32x4*>(uout);
-  if (nv > 0) {
+  if (nv > 0 && staged && loc) {
+    if (fin) {
+      if (fout && uout) move_vec<DT, OP, true, true, true, true, true>(nv, rin, staged, rout, u4);
+      else if (fout) move_vec<DT, OP, true, true, true, false, true>(nv, rin, staged, rout, u4);
+      else move_vec<DT, OP, true, true, false, true, true>(nv, rin, staged, rout, u4);
+    } else {
+      if (fout && uout) move_vec<DT, OP, false, false, true, true, true>(nv, rin, staged, rout, u4);
+      else move_vec<DT, OP, false, false, true, false, true>(nv, rin, staged, rout, u4);
+    }
+  } else if (nv > 0) {
     if (fin && loc) {
       if (fout && uout) move_vec<DT, OP, true, true, true, true>(nv, rin, l4, rout, u4);
       else if (fout) move_vec<DT, OP, true, true, true, false>(nv, rin, l4, rout, u4);
@@ -359,6 +376,9 @@ __device__ __forceinline__ void walk(const RingArgs& a, int r, int c, int w, Uni
   const int N = a.nranks;
   const Range ch = channel_range(a.count, a.nchannels, c, A);
   const int64_t L = ch.hi - ch.lo;
+  // Divisions happen once per loop (or for a ragged tail chunk), never per
+  // stage: the chunk / block index steps down by one each stage.
+  const int k0 = r == 0 ? N - 1 : r - 1;  // chunk of stage 0: (r + N - 1) mod N
   if constexpr (MODE == kAllReduce) {
     // "NCCL" book s. 2.3: a loop covers N chunks; stage j of rank r visits
     // chunk (r + N - 1 - j) mod N: stages 0..N-1 reduce-scatter (stage N-1
@@ -367,12 +387,17 @@ __device__ __forceinline__ void walk(const RingArgs& a, int r, int c, int w, Uni
     for (int64_t off = 0; off < L; off += loop) {
       const int64_t rem = L - off;
       const int64_t cur = ar_loop_chunk(rem, N, a.chunk, A);
+      const int64_t sub_full = align_up(div_up(cur, a.wpc), A);
+      int k = k0;
       for (int j = 0; j < 2 * N - 1; ++j) {
-        const Range ck = ar_chunk(off, rem, cur, ring_chunk(r, N, j));
-        const Range pt = split_part(ck.hi - ck.lo, a.wpc, w, A);
-        const int64_t e0 = ch.lo + ck.lo + pt.lo;
-        unit(pt.hi - pt.lo, j >= 1, j <= N - 1, j <= 2 * N - 3, j >= N - 1, a.send[r] + e0 * E,
-             a.recv[r] + e0 * E);
+        const int64_t clo = min64((int64_t)k * cur, rem);
+        const int64_t n = min64(clo + cur, rem) - clo;
+        const int64_t sub = n == cur ? sub_full : align_up(div_up(n, a.wpc), A);
+        const int64_t plo = min64((int64_t)w * sub, n);
+        const int64_t m = min64(plo + sub, n) - plo;
+        const int64_t e0 = ch.lo + off + clo + plo;
+        unit(m, j >= 1, j <= N - 1, j <= 2 * N - 3, j >= N - 1, a.send[r] + e0 * E, a.recv[r] + e0 * E);
+        k = k == 0 ? N - 1 : k - 1;
       }
     }
   } else if constexpr (MODE == kReduceScatter) {
@@ -381,10 +406,11 @@ __device__ __forceinline__ void walk(const RingArgs& a, int r, int c, int w, Uni
       const int64_t cur = min64(a.chunk, L - off);
       const Range pt = split_part(cur, a.wpc, w, A);
       const int64_t e0 = ch.lo + off + pt.lo;
+      int k = k0;
       for (int j = 0; j < N; ++j) {
-        const int k = ring_chunk(r, N, j);
         unit(pt.hi - pt.lo, j >= 1, true, j <= N - 2, j == N - 1, a.send[r] + ((int64_t)k * a.count + e0) * E,
              a.recv[r] + e0 * E);
+        k = k == 0 ? N - 1 : k - 1;
       }
     }
   } else {
@@ -394,10 +420,11 @@ __device__ __forceinline__ void walk(const RingArgs& a, int r, int c, int w, Uni
       const int64_t cur = min64(a.chunk, L - off);
       const Range pt = split_part(cur, a.wpc, w, A);
       const int64_t e0 = ch.lo + off + pt.lo;
+      int b = r;
       for (int j = 0; j < N; ++j) {
-        const int b = ag_block(r, N, j);
         unit(pt.hi - pt.lo, j >= 1, j == 0, j <= N - 2, true, a.send[r] + e0 * E,
              a.recv[r] + ((int64_t)b * a.count + e0) * E);
+        b = b == 0 ? N - 1 : b - 1;
       }
     }
   }
@@ -434,10 +461,140 @@ __device__ __forceinline__ Pipe locate(const RingArgs& a) {
 // Bulk kernel
 // ---------------------------------------------------------------------------
 
+// Schedule iterator: the same walk as walk<>() (which the flag-packed kernel
+// uses), one FIFO slot step at a time, so that the bulk kernel can look one
+// step ahead. Empty units produce no step.
+template <int DT, int MODE>
+struct StepIter {
+  static constexpr int64_t E = sizeof(typename Elem<DT>::T);
+  static constexpr int64_t A = 16 / E;
+  // fixed per workgroup
+  const char* send_r;
+  char* recv_r;
+  int64_t count, chunk, L, ch_lo, slice;
+  int N, r, w, wpc;
+  // loop and stage
+  int64_t off, rem, cur, sub_full, part_lo, part_n;
+  int j, idx;
+  // current unit and step
+  int64_t m, s, local_e, out_e;
+  bool recv, use_local, send, store, done;
+
+  __device__ __forceinline__ int nstages() const { return MODE == kAllReduce ? 2 * N - 1 : N; }
+
+  __device__ __forceinline__ void begin_loop() {
+    rem = L - off;
+    if constexpr (MODE == kAllReduce) {
+      cur = ar_loop_chunk(rem, N, chunk, A);
+      sub_full = align_up(div_up(cur, wpc), A);
+    } else {
+      cur = min64(chunk, rem);
+      const Range pt = split_part(cur, wpc, w, A);
+      part_lo = pt.lo;
+      part_n = pt.hi - pt.lo;
+    }
+    j = 0;
+    idx = MODE == kAllGather ? r : (r == 0 ? N - 1 : r - 1);
+  }
+
+  __device__ __forceinline__ void set_unit() {
+    s = 0;
+    if constexpr (MODE == kAllReduce) {
+      const int64_t clo = min64((int64_t)idx * cur, rem);
+      const int64_t n = min64(clo + cur, rem) - clo;
+      const int64_t sub = n == cur ? sub_full : align_up(div_up(n, wpc), A);
+      const int64_t plo = min64((int64_t)w * sub, n);
+      m = min64(plo + sub, n) - plo;
+      local_e = out_e = ch_lo + off + clo + plo;
+      recv = j >= 1;
+      use_local = j <= N - 1;
+      send = j <= 2 * N - 3;
+      store = j >= N - 1;
+    } else if constexpr (MODE == kReduceScatter) {
+      m = part_n;
+      out_e = ch_lo + off + part_lo;
+      local_e = (int64_t)idx * count + out_e;
+      recv = j >= 1;
+      use_local = true;
+      send = j <= N - 2;
+      store = j == N - 1;
+    } else {
+      m = part_n;
+      local_e = ch_lo + off + part_lo;
+      out_e = (int64_t)idx * count + local_e;
+      recv = j >= 1;
+      use_local = j == 0;
+      send = j <= N - 2;
+      store = true;
+    }
+  }
+
+  // Moves to the next stage (and loop) until a non-empty unit or the end.
+  __device__ __forceinline__ void next_unit() {
+    do {
+      ++j;
+      idx = idx == 0 ? N - 1 : idx - 1;
+      if (j == nstages()) {
+        off += MODE == kAllReduce ? (int64_t)N * chunk : chunk;
+        if (off >= L) {
+          done = true;
+          return;
+        }
+        begin_loop();
+      }
+      set_unit();
+    } while (m == 0);
+  }
+
+  __device__ __forceinline__ void init(const RingArgs& a, int rank, int c, int part) {
+    N = a.nranks;
+    r = rank;
+    w = part;
+    wpc = a.wpc;
+    count = a.count;
+    chunk = a.chunk;
+    slice = a.slot_bytes / E;
+    send_r = a.send[r];
+    recv_r = a.recv[r];
+    const Range ch = channel_range(a.count, a.nchannels, c, A);
+    ch_lo = ch.lo;
+    L = ch.hi - ch.lo;
+    off = 0;
+    done = L <= 0;
+    if (done) return;
+    begin_loop();
+    set_unit();
+    if (m == 0) next_unit();
+  }
+
+  __device__ __forceinline__ void next() {
+    s += slice;
+    if (s < m) return;
+    next_unit();
+  }
+
+  __device__ __forceinline__ int64_t ns() const { return min64(slice, m - s); }
+  __device__ __forceinline__ const char* local() const { return send_r + (local_e + s) * E; }
+  __device__ __forceinline__ char* out() const { return recv_r + (out_e + s) * E; }
+};
+
+// Stages the whole-vector part of a step's own operand into LDS with
+// direct-to-LDS 128-bit loads (gfx950): lane i of a wave writes 16 bytes at
+// the wave's base + 16 i, so LDS holds the same layout as memory.
+__device__ __forceinline__ void stage_to_lds(const char* src, int64_t nv, u32x4* lds) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t i = threadIdx.x; i < nv; i += kThreads) {
+    auto g = (__attribute__((address_space(1))) void*)(const_cast<char*>(src) + i * 16);
+    auto l = (__attribute__((address_space(3))) void*)(lds + (i - lane));
+    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+  }
+}
+
 template <int DT, int OP, int MODE>
 __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
-  constexpr int64_t E = sizeof(T);
+  constexpr int64_t A = 16 / (int64_t)sizeof(T);
+  extern __shared__ u32x4 lds_stage[];  // [2][slot_bytes / 16] when a.lds_stage
   const Pipe p = locate(a);
   if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
   __shared__ uint64_t s_base[2];
@@ -450,47 +607,73 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   const uint64_t in_base = s_base[0];
   const uint64_t out_base = s_base[1];
   const uint64_t nslots = (uint64_t)a.nslots;
-  const int64_t slice = a.slot_bytes / E;
+  const int64_t stage_vecs = a.slot_bytes / 16;
   uint64_t nrecv = 0, nsent = 0;
   uint64_t known_tail = 0, known_head = 0;  // meaningful in thread 0 only
   bool stop = false;                         // thread 0: stop waiting
   const WaitCtx wc = wait_ctx(a);
+  // Slot of the next receive / send: (base + count) mod nslots, advanced
+  // without a division.
+  uint32_t in_slot = (uint32_t)(in_base % nslots);
+  uint32_t out_slot = (uint32_t)(out_base % nslots);
 
-  walk<DT, MODE>(a, p.r, p.c, p.w,
-                 [&](int64_t m, bool recv, bool use_local, bool send, bool store, const char* local, char* out) {
-    for (int64_t s = 0; s < m; s += slice) {
-      const int64_t ns = min64(slice, m - s);
-      if (threadIdx.x == 0 && !stop) {
-        // A counter value seen earlier may already cover this step. The
-        // barrier below keeps every thread's slot accesses after the wait.
-        const uint64_t need_tail = in_base + nrecv + 1;
-        if (recv && known_tail < need_tail) {
-          known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
-          stop = known_tail == 0;
-        }
-        const uint64_t need_head = out_base + nsent + 1 - nslots;
-        if (!stop && send && nsent + 1 > nslots && known_head < need_head) {
-          known_head = wait_geq(&p.out_ctr->head, need_head, wc);
-          stop = known_head == 0;
-        }
+  StepIter<DT, MODE> it;
+  it.init(a, p.r, p.c, p.w);
+  StepIter<DT, MODE> nx = it;
+  if (!nx.done) nx.next();
+  const bool lds = a.lds_stage && a.vec_ok;
+  int buf = 0;
+  if (lds && !it.done && it.use_local) {
+    stage_to_lds(it.local(), it.ns() / A, lds_stage);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  while (!it.done) {
+    const bool recv = it.recv, send = it.send;
+    if (threadIdx.x == 0 && !stop) {
+      // A counter value seen earlier may already cover this step. The
+      // barrier below keeps every thread's slot accesses after the wait.
+      const uint64_t need_tail = in_base + nrecv + 1;
+      if (recv && known_tail < need_tail) {
+        known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
+        stop = known_tail == 0;
       }
-      __syncthreads();
-      const char* fin = recv ? p.in_fifo + ((in_base + nrecv) % nslots) * a.slot_bytes : nullptr;
-      char* fout = send ? p.out_fifo + ((out_base + nsent) % nslots) * a.slot_bytes : nullptr;
-      move_slice<DT, OP>(ns, fin, use_local ? local + s * E : nullptr, fout, store ? out + s * E : nullptr,
-                         a.slot_bytes, a.vec_ok);
-      // Every thread's FIFO stores (device-coherent) and FIFO loads have
-      // completed before thread 0 publishes the new tail and head.
-      wait_vmem();
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        if (send) st_relaxed(&p.out_ctr->tail, out_base + nsent + 1);
-        if (recv) st_relaxed(&p.in_ctr->head, in_base + nrecv + 1);
+      const uint64_t need_head = out_base + nsent + 1 - nslots;
+      if (!stop && send && nsent + 1 > nslots && known_head < need_head) {
+        known_head = wait_geq(&p.out_ctr->head, need_head, wc);
+        stop = known_head == 0;
       }
-      nrecv += recv ? 1 : 0;
-      nsent += send ? 1 : 0;
     }
-  });
+    __syncthreads();
+    const int64_t ns = it.ns();
+    const char* fin = recv ? p.in_fifo + (int64_t)in_slot * a.slot_bytes : nullptr;
+    char* fout = send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr;
+    move_slice<DT, OP>(ns, fin, it.use_local ? it.local() : nullptr, fout, it.store ? it.out() : nullptr,
+                       a.slot_bytes, a.vec_ok, lds && it.use_local ? lds_stage + buf * stage_vecs : nullptr);
+    // The next step's own operand streams into the other LDS buffer while
+    // this step's stores drain.
+    if (lds && !nx.done && nx.use_local) stage_to_lds(nx.local(), nx.ns() / A, lds_stage + (buf ^ 1) * stage_vecs);
+    // Every thread's FIFO stores (device-coherent), FIFO loads and staging
+    // loads have completed before thread 0 publishes the new tail and head.
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (send) st_relaxed(&p.out_ctr->tail, out_base + nsent + 1);
+      if (recv) st_relaxed(&p.in_ctr->head, in_base + nrecv + 1);
+    }
+    if (recv) {
+      ++nrecv;
+      in_slot = in_slot + 1 == (uint32_t)nslots ? 0 : in_slot + 1;
+    }
+    if (send) {
+      ++nsent;
+      out_slot = out_slot + 1 == (uint32_t)nslots ? 0 : out_slot + 1;
+    }
+    buf ^= 1;
+    it = nx;
+    if (!nx.done) nx.next();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -691,7 +874,8 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
 template <int DT, int OP, int MODE>
 static hipError_t launch_bulk_t(const RingArgs& a, hipStream_t s) {
   const int grid = a.nranks * a.nchannels * a.wpc;
-  hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+  const size_t lds = a.lds_stage ? 2 * (size_t)a.slot_bytes : 0;
+  hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -765,23 +949,23 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
 }
 
 template <typename K>
-static int occ(K k) {
+static int occ(K k, size_t lds) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, lds) != hipSuccess) return 0;
   return n;
 }
 
-int ring_blocks_per_cu() {
+int ring_blocks_per_cu(size_t bulk_lds_bytes) {
   int m = 1 << 30;
   auto acc = [&](int v) { m = v < m ? v : m; };
 #define RS_OCC_DT(DT)                                                                 \
-  acc(occ(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce>));                            \
-  acc(occ(ring_bulk_kernel<DT, RINGSIM_MAX, kAllReduce>));                            \
-  acc(occ(ring_bulk_kernel<DT, RINGSIM_PROD, kReduceScatter>));                       \
-  acc(occ(ring_bulk_kernel<DT, RINGSIM_SUM, kAllGather>));                            \
-  acc(occ(ring_flag_kernel<DT, RINGSIM_SUM, kAllReduce>));                            \
-  acc(occ(ring_flag_kernel<DT, RINGSIM_MIN, kReduceScatter>));                        \
-  acc(occ(ring_flag_kernel<DT, RINGSIM_SUM, kAllGather>));
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce>, bulk_lds_bytes));            \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_MAX, kAllReduce>, bulk_lds_bytes));            \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_PROD, kReduceScatter>, bulk_lds_bytes));       \
+  acc(occ(ring_bulk_kernel<DT, RINGSIM_SUM, kAllGather>, bulk_lds_bytes));            \
+  acc(occ(ring_flag_kernel<DT, RINGSIM_SUM, kAllReduce>, 0));                         \
+  acc(occ(ring_flag_kernel<DT, RINGSIM_MIN, kReduceScatter>, 0));                     \
+  acc(occ(ring_flag_kernel<DT, RINGSIM_SUM, kAllGather>, 0));
   RS_OCC_DT(RINGSIM_INT32)
   RS_OCC_DT(RINGSIM_INT64)
   RS_OCC_DT(RINGSIM_FLOAT32)
