@@ -217,6 +217,58 @@ def copy_calibration(args) -> int:
     return 0 if ok else 1
 
 
+def size_sweep(args) -> int:
+    """Latency / bandwidth of the 16-rank int32 all-reduce across message
+    sizes; flag-packed protocol below 64 KiB per rank, bulk above (auto)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import ring_all_reduce_allreduce_amd as rs
+    import synth
+
+    n, nch = 16, 16
+    comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None)
+    size = 8
+    k = 0
+    while size <= args.sweep_max_bytes:
+        count = size // 4
+        send = synth.device_inputs(4, n, count, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
+        recv = [torch.empty_like(t) for t in send]
+        for _ in range(args.warmup):
+            rs.allreduce(comm, send, recv)
+        torch.cuda.synchronize()
+        idx = np.unique(np.linspace(0, count - 1, min(count, 4096)).astype(np.int64))
+        cols = [t.cpu().numpy()[idx] if count <= (1 << 22) else t[torch.from_numpy(idx).cuda()].cpu().numpy()
+                for t in send]
+        ok = bool(np.array_equal(recv[k % n][torch.from_numpy(idx).cuda()].cpu().numpy(),
+                                 oracle.ring_allreduce(cols, "sum", "int32", nchannels=1)[0]))
+        steps = args.steps if size < (64 << 20) else max(5, args.steps // 4)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(2_000_000)
+        for i in range(steps):
+            starts[i].record()
+            rs.allreduce(comm, send, recv)
+            ends[i].record()
+        torch.cuda.synchronize()
+        t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
+        proto = "flag" if (args.proto == "flag" or (args.proto == "auto" and size < 65536)) else "bulk"
+        busbw = size / t * bus_factor("allreduce", n) / 1e9
+        byts = algorithmic_bytes("allreduce", n, size) * (1 if proto == "bulk" else 1)
+        print(json.dumps({"bytes_per_rank": size, "proto": proto, "us": round(t * 1e6, 2),
+                          "busbw_gbs": round(busbw, 3), "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
+                          "sampled_parity": ok}), flush=True)
+        if not ok:
+            return 1
+        del send, recv
+        size *= 2
+        k += 1
+    rs.comm_destroy(comm)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +280,11 @@ def main() -> int:
     ap.add_argument("--wpc", type=int, default=0, help="workgroups per channel (0 = library default)")
     ap.add_argument("--slot-bytes", type=int, default=0)
     ap.add_argument("--nslots", type=int, default=0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="message-size sweep instead (16 ranks, int32, 8 B .. 256 MiB per rank, 16 channels, "
+                         "auto protocol): one JSON line per size")
+    ap.add_argument("--sweep-max-bytes", type=int, default=256 << 20)
+    ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time the library's copy kernel on 1 GiB (a one-rank all-to-all) instead; used to "
                          "scale the HBM byte counters")
@@ -245,6 +302,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration(args)
+    if args.sweep:
+        return size_sweep(args)
 
     w = WORKLOADS[args.workload]
     n, dtype, coll = w["nranks"], w["dtype"], w["coll"]

@@ -184,8 +184,8 @@ __device__ __forceinline__ bool host_abort_seen(const WaitCtx& w) {
   return __hip_atomic_load(w.host_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u;
 }
 
-__device__ __forceinline__ bool abort_seen(const WaitCtx& w) {
-  return __hip_atomic_load(w.dev_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || host_abort_seen(w);
+__device__ __forceinline__ bool dev_abort_seen(const WaitCtx& w) {
+  return __hip_atomic_load(w.dev_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
 // Records the first error in the host-visible word and tells every other
@@ -195,10 +195,16 @@ __device__ __forceinline__ void raise_error(WaitCtx w, uint32_t code) {
   __hip_atomic_store(w.dev_abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Checked every 256 spins: abort word, then the time bound.
-__device__ __forceinline__ bool give_up(const WaitCtx& w, uint64_t t0) {
-  if (abort_seen(w)) {
-    raise_error(w, host_abort_seen(w) ? kErrAborted : kErrTimeout);
+// Called from spin loops with the spin count. Every 256 spins: the device
+// abort word (another workgroup gave up; its error is already recorded) and
+// the time bound. Every 16384 spins (about a millisecond of spinning): the
+// host-mapped abort word -- reading host memory is a round trip over the
+// host link, too slow and too contended to do on every miss.
+__device__ __forceinline__ bool give_up(const WaitCtx& w, uint64_t t0, uint32_t it) {
+  if (it & 255u) return false;
+  if (dev_abort_seen(w)) return true;
+  if ((it & 16383u) == 0u && host_abort_seen(w)) {
+    raise_error(w, kErrAborted);
     return true;
   }
   if (wall_clock64() - t0 > w.timeout_ticks) {
@@ -213,17 +219,13 @@ __device__ __forceinline__ bool give_up(const WaitCtx& w, uint64_t t0) {
 __device__ __forceinline__ uint64_t wait_geq(const uint64_t* p, uint64_t target, WaitCtx w) {
   uint64_t v = ld_relaxed(p);
   if (v >= target) return v;
-  if (abort_seen(w)) {
-    raise_error(w, host_abort_seen(w) ? kErrAborted : kErrTimeout);
-    return 0;
-  }
   const uint64_t t0 = wall_clock64();
   uint32_t it = 0;
   while (true) {
     __builtin_amdgcn_s_sleep(1);
     v = ld_relaxed(p);
     if (v >= target) return v;
-    if ((++it & 255u) == 0u && give_up(w, t0)) return 0;
+    if (give_up(w, t0, ++it)) return 0;
   }
 }
 
@@ -690,7 +692,7 @@ __device__ __forceinline__ u32x2 poll_line(const uint64_t* line, uint32_t flag, 
     const uint64_t t0 = wall_clock64();
     uint32_t it = 0;
     while ((uint32_t)(v0 >> 32) != flag || (uint32_t)(v1 >> 32) != flag) {
-      if ((++it & 255u) == 0u && give_up(w, t0)) {
+      if (give_up(w, t0, ++it)) {
         stop = true;
         break;
       }
