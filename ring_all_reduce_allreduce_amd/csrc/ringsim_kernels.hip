@@ -85,19 +85,29 @@ __device__ __forceinline__ uint64_t op_i64(uint64_t a, uint64_t b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two float32 values -> packed bfloat16 pair, round to nearest even, with
+// gfx950's conversion instruction (v_cvt_pk_bf16_f32: both halves at once).
+__device__ __forceinline__ uint32_t to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Two bf16 values packed in a 32-bit word: each computed in fp32, rounded once.
+__device__ __forceinline__ uint32_t to_bf16(float f) { return to_bf16x2(f, 0.0f) & 0xffffu; }
+
+// Two bf16 values packed in a 32-bit word. Sum and product are computed in
+// fp32 and rounded once; max and min pick one of the operands' halves (the
+// result is exact), with -0 below +0.
 template <int OP>
 __device__ __forceinline__ uint32_t op_bf16x2(uint32_t a, uint32_t b) {
-  const uint32_t lo = to_bf16(op_f32<OP>(bf16_lo(a), bf16_lo(b)));
-  const uint32_t hi = to_bf16(op_f32<OP>(bf16_hi(a), bf16_hi(b)));
-  return lo | (hi << 16);
+  if constexpr (OP == RINGSIM_SUM || OP == RINGSIM_PROD) {
+    return to_bf16x2(op_f32<OP>(bf16_lo(a), bf16_lo(b)), op_f32<OP>(bf16_hi(a), bf16_hi(b)));
+  } else {
+    const uint32_t lo = __float_as_uint(op_f32<OP>(bf16_lo(a), bf16_lo(b))) >> 16;
+    const uint32_t hi = __float_as_uint(op_f32<OP>(bf16_hi(a), bf16_hi(b))) & 0xffff0000u;
+    return lo | hi;
+  }
 }
 
 template <int DT>
@@ -147,7 +157,7 @@ struct VOp {
     if constexpr (DT == RINGSIM_INT64) {
       return op_i64<OP>(a, b);
     } else if constexpr (DT == RINGSIM_BFLOAT16) {
-      return (T)to_bf16(op_f32<OP>(bf16_lo(a), bf16_lo(b)));
+      return (T)(op_bf16x2<OP>(a, b) & 0xffffu);
     } else {
       return word(a, b);
     }

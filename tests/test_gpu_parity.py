@@ -221,3 +221,38 @@ def test_workload2_full_size():
     st = np.stack(xs).astype(np.float64)
     err = np.abs(got[3].astype(np.float64) - st.sum(axis=0))
     assert np.all(err <= 1e-6 * np.abs(st).sum(axis=0))
+
+
+def _random_float_bits(rng, count, dtype, exp_lo, exp_hi):
+    """Finite values with random sign, mantissa and biased exponent in
+    [exp_lo, exp_hi]; exponent 0 gives subnormals and signed zeros."""
+    if dtype == "float32":
+        mant = rng.integers(0, 1 << 23, count, dtype=np.uint64)
+        exp = rng.integers(exp_lo, exp_hi + 1, count, dtype=np.uint64)
+        sign = rng.integers(0, 2, count, dtype=np.uint64)
+        bits = (sign << 31) | (exp << 23) | mant
+        bits[::97] = 0                      # +0
+        bits[1::97] = 1 << 31               # -0
+        return bits.astype(np.uint32).view(np.float32)
+    mant = rng.integers(0, 1 << 7, count, dtype=np.uint32)
+    exp = rng.integers(exp_lo, exp_hi + 1, count, dtype=np.uint32)
+    sign = rng.integers(0, 2, count, dtype=np.uint32)
+    bits = (sign << 15) | (exp << 7) | mant
+    bits[::97] = 0
+    bits[1::97] = 1 << 15
+    return bits.astype(np.uint16)
+
+
+@pytest.mark.parametrize("proto", ["bulk", "flag"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_allreduce_random_bit_patterns(proto, dtype):
+    """Subnormals, signed zeros, ties and wide exponent ranges: every hop must
+    round exactly like the oracle (no flush to zero, no fused operations)."""
+    rng = np.random.default_rng(2024)
+    n, count, nch = 5, 20_011, 3
+    for op, (lo, hi) in (("sum", (0, 200)), ("max", (0, 254)), ("min", (0, 254)), ("prod", (120, 134)),
+                         ("sum", (0, 3))):
+        xs = [_random_float_bits(rng, count, dtype, lo, hi) for _ in range(n)]
+        got = _run_allreduce(xs, dtype, op, nch, proto, chunk_bytes=16384)
+        want = oracle.ring_allreduce(xs, op, dtype, nchannels=nch, chunk_bytes=16384)
+        _assert_same(got, want, dtype, f"{dtype} {op} exponents {lo}..{hi}")
