@@ -218,8 +218,9 @@ def copy_calibration(args) -> int:
 
 
 def size_sweep(args) -> int:
-    """Latency / bandwidth of the 16-rank int32 all-reduce across message
-    sizes; flag-packed protocol below 64 KiB per rank, bulk above (auto)."""
+    """Latency / bandwidth of the int32 all-reduce across message sizes
+    (default 16 ranks, 16 channels); AUTO picks the protocol per size with the
+    library's cost model, and each line reports the protocol it ran."""
     import numpy as np
     import torch
 
@@ -227,7 +228,7 @@ def size_sweep(args) -> int:
     import ring_all_reduce_allreduce_amd as rs
     import synth
 
-    n, nch = 16, 16
+    n, nch = args.sweep_ranks, args.sweep_channels
     comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None)
     size = 8
     k = 0
@@ -254,10 +255,11 @@ def size_sweep(args) -> int:
             ends[i].record()
         torch.cuda.synchronize()
         t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
-        proto = "flag" if (args.proto == "flag" or (args.proto == "auto" and size < 65536)) else "bulk"
+        proto = {1: "bulk", 2: "flag"}.get(rs.comm_query(comm)["last_proto"], "?")
         busbw = size / t * bus_factor("allreduce", n) / 1e9
-        byts = algorithmic_bytes("allreduce", n, size) * (1 if proto == "bulk" else 1)
-        print(json.dumps({"bytes_per_rank": size, "proto": proto, "us": round(t * 1e6, 2),
+        byts = algorithmic_bytes("allreduce", n, size)
+        print(json.dumps({"nranks": n, "nchannels": nch, "bytes_per_rank": size, "proto": proto,
+                          "us": round(t * 1e6, 2),
                           "busbw_gbs": round(busbw, 3), "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
                           "sampled_parity": ok}), flush=True)
         if not ok:
@@ -284,6 +286,8 @@ def main() -> int:
                     help="message-size sweep instead (16 ranks, int32, 8 B .. 256 MiB per rank, 16 channels, "
                          "auto protocol): one JSON line per size")
     ap.add_argument("--sweep-max-bytes", type=int, default=256 << 20)
+    ap.add_argument("--sweep-ranks", type=int, default=16)
+    ap.add_argument("--sweep-channels", type=int, default=16)
     ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time the library's copy kernel on 1 GiB (a one-rank all-to-all) instead; used to "

@@ -92,8 +92,12 @@ typedef enum {
 
 /* Protocols ("NCCL" book, s. 2.4): BULK keeps readiness in separate step
  * counters (Simple); FLAG packs a 4-byte flag with every 4 bytes of payload
- * so the receiver polls the data itself (LL). AUTO picks FLAG below
- * flag_threshold_bytes per rank, BULK otherwise. */
+ * so the receiver polls the data itself (LL). AUTO picks the protocol with
+ * the lower predicted time (ringsim_debug_model), or FLAG below
+ * flag_threshold_bytes per rank when a threshold is configured. FLAG uses a
+ * chunk of min(chunk_bytes, 64 KiB); AUTO only picks it for all-reduces whose
+ * per-channel share fits one tail loop either way, so AUTO's results do not
+ * depend on the protocol it picks. */
 typedef enum {
   RINGSIM_PROTO_AUTO = 0,
   RINGSIM_PROTO_BULK = 1,
@@ -114,7 +118,7 @@ typedef struct {
   size_t slot_bytes;           /* bulk FIFO slot; default 32768; multiple of 4096 */
   int nslots;                  /* bulk FIFO depth; default 8 (NCCL_STEPS) */
   int timeout_ms;              /* bound on any single wait; default 10000, env RINGSIM_TIMEOUT_MS */
-  size_t flag_threshold_bytes; /* AUTO: FLAG below this many bytes per rank; default 65536 */
+  size_t flag_threshold_bytes; /* AUTO: FLAG below this many bytes per rank; default 0 = cost model */
 } ringsim_config_t;
 
 /* Read-only description of a communicator. */
@@ -133,6 +137,7 @@ typedef struct {
   int max_resident_workgroups; /* co-resident workgroups the device can hold */
   int compute_units;
   uint64_t calls;              /* collective calls enqueued so far */
+  int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG, 0 if none */
 } ringsim_comm_info_t;
 
 /* Fills *cfg with the defaults. Environment overrides, read by this call:
@@ -202,6 +207,16 @@ ringsim_result_t ringsim_abort(ringsim_comm_t comm);
 
 /* Static text for a result code. */
 const char* ringsim_get_error_string(ringsim_result_t result);
+
+/* Host-only cost model behind AUTO ("NCCL" book, ch. 5, ring.cc: latency =
+ * hops x per-hop latency, bandwidth term = bytes moved / achievable bandwidth,
+ * the flag protocol moving twice the FIFO bytes), with constants measured on
+ * MI355X. Writes the predicted microseconds of one call of `coll`
+ * (RINGSIM_COLL_ALLREDUCE, _REDUCE_SCATTER or _ALL_GATHER) with
+ * `bytes_per_rank` bytes per rank (all-reduce buffer, reduce-scatter input,
+ * all-gather output) on each protocol. Touches no device. */
+ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t bytes_per_rank, double* us_bulk,
+                                     double* us_flag);
 
 /* Host-only view of the partition used by the kernels. For `coll`
  * (ringsim_coll_t), writes rows of 5 int64 values

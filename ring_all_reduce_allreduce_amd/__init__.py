@@ -85,6 +85,7 @@ class CommInfo(ctypes.Structure):
         ("max_resident_workgroups", ctypes.c_int),
         ("compute_units", ctypes.c_int),
         ("calls", ctypes.c_uint64),
+        ("last_proto", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:
@@ -120,6 +121,7 @@ def lib() -> ctypes.CDLL:
         "ringsim_abort": (res, [vp]),
         "ringsim_get_error_string": (ctypes.c_char_p, [res]),
         "ringsim_debug_plan": (res, [i, sz, i, i, sz, i, ctypes.POINTER(ctypes.c_int64), sz, ctypes.POINTER(sz)]),
+        "ringsim_debug_model": (res, [i, i, i, sz, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (rt, args) in sig.items():
         f = getattr(L, name)
@@ -277,6 +279,15 @@ def get_async_error(comm: Comm) -> int:
 
 def abort(comm: Comm) -> None:
     _check(lib().ringsim_abort(comm), "ringsim_abort")
+
+
+def debug_model(coll: str | int, nranks: int, nchannels: int, bytes_per_rank: int) -> dict:
+    """Predicted microseconds per protocol (host-only cost model behind AUTO)."""
+    c = COLLS[coll] if isinstance(coll, str) else int(coll)
+    b, f = ctypes.c_double(), ctypes.c_double()
+    _check(lib().ringsim_debug_model(c, nranks, nchannels, bytes_per_rank, ctypes.byref(b), ctypes.byref(f)),
+           "ringsim_debug_model")
+    return {"bulk_us": b.value, "flag_us": f.value}
 
 
 def debug_plan(coll: str | int, count: int, nranks: int, nchannels: int, chunk_bytes: int, dtype: str | int):

@@ -18,6 +18,7 @@
 #include <new>
 #include <unordered_set>
 
+#include "ring_model.h"
 #include "ring_plan.h"
 #include "ringsim_internal.h"
 
@@ -89,6 +90,7 @@ struct ringsim_comm {
   uint32_t* host_words;      // [0] abort request, [1] kernel error (host view)
   uint32_t* host_words_dev;  // the same words as the device sees them
   uint64_t calls;
+  int last_proto;
   ringsim_result_t sticky;
   hipStream_t last_stream;
   bool has_last_stream;
@@ -168,10 +170,23 @@ void fill_common(const ringsim_comm* c, RingArgs* a, const void* const* sb, void
   a->skip_rank = c->skip_rank;
 }
 
+// AUTO's choice: a fixed threshold when one was configured, else the cost
+// model. The flag protocol caps its chunk at kFlagChunkBytes; it is only
+// chosen while every channel's share fits in one tail loop under both chunk
+// sizes, so the partition -- and every floating-point result -- is the same
+// whichever protocol runs.
+bool auto_picks_flag(const ringsim_comm* c, int mode, size_t bytes_per_rank) {
+  if (c->flag_threshold) return bytes_per_rank < c->flag_threshold;
+  const size_t limit = (size_t)c->nranks * c->nchannels * std::min<size_t>(c->chunk_bytes, kFlagChunkBytes);
+  if (mode == kAllReduce && bytes_per_rank >= limit) return false;
+  const RingModel m;
+  return model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, true) <
+         model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, false);
+}
+
 // Picks the protocol and fills the protocol-dependent launch geometry.
-void fill_proto(const ringsim_comm* c, RingArgs* a, size_t bytes_per_rank, int esize, bool* flag) {
-  bool f = c->proto == RINGSIM_PROTO_FLAG ||
-           (c->proto == RINGSIM_PROTO_AUTO && bytes_per_rank < c->flag_threshold);
+void fill_proto(const ringsim_comm* c, RingArgs* a, int mode, size_t bytes_per_rank, int esize, bool* flag) {
+  const bool f = c->proto == RINGSIM_PROTO_FLAG || (c->proto == RINGSIM_PROTO_AUTO && auto_picks_flag(c, mode, bytes_per_rank));
   *flag = f;
   if (f) {
     a->wpc = 1;
@@ -234,10 +249,11 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   a.count = (int64_t)count;
   const size_t per_rank_bytes = (mode == kAllReduce ? count : count * n) * esize;
   bool flag = false;
-  fill_proto(c, &a, per_rank_bytes, esize, &flag);
+  fill_proto(c, &a, mode, per_rank_bytes, esize, &flag);
   // Vector moves need every unit to start on a 16-byte boundary; for the
   // block-strided collectives that requires whole 16-byte blocks.
   a.vec_ok = vec && (mode == kAllReduce || (count * esize) % 16 == 0);
+  c->last_proto = flag ? RINGSIM_PROTO_FLAG : RINGSIM_PROTO_BULK;
   const hipError_t e = flag ? launch_ring_flag(a, mode, dtype, op, s) : launch_ring_bulk(a, mode, dtype, op, s);
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "kernel launch failed: %s", hipGetErrorString(e));
@@ -270,7 +286,7 @@ ringsim_result_t ringsim_config_default(ringsim_config_t* cfg) {
   cfg->slot_bytes = (size_t)env_long("RINGSIM_SLOT_BYTES", kDefaultSlotBytes);
   cfg->nslots = (int)env_long("RINGSIM_NSLOTS", kDefaultSlots);
   cfg->timeout_ms = (int)env_long("RINGSIM_TIMEOUT_MS", 10000);
-  cfg->flag_threshold_bytes = (size_t)env_long("RINGSIM_FLAG_THRESHOLD", 65536);
+  cfg->flag_threshold_bytes = (size_t)env_long("RINGSIM_FLAG_THRESHOLD", 0);
   return RINGSIM_SUCCESS;
 }
 
@@ -430,6 +446,7 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
   info->max_resident_workgroups = comm->blocks_per_cu * comm->compute_units;
   info->compute_units = comm->compute_units;
   info->calls = comm->calls;
+  info->last_proto = comm->last_proto;
   return RINGSIM_SUCCESS;
 }
 
@@ -520,6 +537,18 @@ const char* ringsim_get_error_string(ringsim_result_t result) {
     case RINGSIM_ABORTED: return "communicator aborted";
     default: return "unknown result code";
   }
+}
+
+ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t bytes_per_rank, double* us_bulk,
+                                     double* us_flag) {
+  if (!us_bulk || !us_flag) return RINGSIM_INVALID_ARGUMENT;
+  if (coll < RINGSIM_COLL_ALLREDUCE || coll > RINGSIM_COLL_ALL_GATHER) return RINGSIM_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS)
+    return RINGSIM_INVALID_ARGUMENT;
+  const RingModel m;
+  *us_bulk = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, false);
+  *us_flag = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, true);
+  return RINGSIM_SUCCESS;
 }
 
 ringsim_result_t ringsim_debug_plan(int coll, size_t count, int nranks, int nchannels, size_t chunk_bytes,

@@ -375,73 +375,6 @@ __device__ __forceinline__ void move_slice(int64_t n, const char* fin, const cha
   }
 }
 
-// ---------------------------------------------------------------------------
-// Schedule walker: calls unit(m, recv, use_local, send, store, local, out)
-// for every unit of workgroup (r, c, w) in FIFO order.
-// ---------------------------------------------------------------------------
-
-template <int DT, int MODE, typename Unit>
-__device__ __forceinline__ void walk(const RingArgs& a, int r, int c, int w, Unit&& unit) {
-  using T = typename Elem<DT>::T;
-  constexpr int64_t E = sizeof(T);
-  constexpr int64_t A = 16 / E;
-  const int N = a.nranks;
-  const Range ch = channel_range(a.count, a.nchannels, c, A);
-  const int64_t L = ch.hi - ch.lo;
-  // Divisions happen once per loop (or for a ragged tail chunk), never per
-  // stage: the chunk / block index steps down by one each stage.
-  const int k0 = r == 0 ? N - 1 : r - 1;  // chunk of stage 0: (r + N - 1) mod N
-  if constexpr (MODE == kAllReduce) {
-    // "NCCL" book s. 2.3: a loop covers N chunks; stage j of rank r visits
-    // chunk (r + N - 1 - j) mod N: stages 0..N-1 reduce-scatter (stage N-1
-    // completes chunk r), stages N-1..2N-2 store, stages 0..2N-3 forward.
-    const int64_t loop = (int64_t)N * a.chunk;
-    for (int64_t off = 0; off < L; off += loop) {
-      const int64_t rem = L - off;
-      const int64_t cur = ar_loop_chunk(rem, N, a.chunk, A);
-      const int64_t sub_full = align_up(div_up(cur, a.wpc), A);
-      int k = k0;
-      for (int j = 0; j < 2 * N - 1; ++j) {
-        const int64_t clo = min64((int64_t)k * cur, rem);
-        const int64_t n = min64(clo + cur, rem) - clo;
-        const int64_t sub = n == cur ? sub_full : align_up(div_up(n, a.wpc), A);
-        const int64_t plo = min64((int64_t)w * sub, n);
-        const int64_t m = min64(plo + sub, n) - plo;
-        const int64_t e0 = ch.lo + off + clo + plo;
-        unit(m, j >= 1, j <= N - 1, j <= 2 * N - 3, j >= N - 1, a.send[r] + e0 * E, a.recv[r] + e0 * E);
-        k = k == 0 ? N - 1 : k - 1;
-      }
-    }
-  } else if constexpr (MODE == kReduceScatter) {
-    // Block b is folded b+1, ..., b and lands on rank b (stage N-1).
-    for (int64_t off = 0; off < L; off += a.chunk) {
-      const int64_t cur = min64(a.chunk, L - off);
-      const Range pt = split_part(cur, a.wpc, w, A);
-      const int64_t e0 = ch.lo + off + pt.lo;
-      int k = k0;
-      for (int j = 0; j < N; ++j) {
-        unit(pt.hi - pt.lo, j >= 1, true, j <= N - 2, j == N - 1, a.send[r] + ((int64_t)k * a.count + e0) * E,
-             a.recv[r] + e0 * E);
-        k = k == 0 ? N - 1 : k - 1;
-      }
-    }
-  } else {
-    // All-gather, "NCCL 专家课程 17" (Bootstrap Ring 与 AllGather): round j
-    // sends block (r - j) and receives block (r - j - 1).
-    for (int64_t off = 0; off < L; off += a.chunk) {
-      const int64_t cur = min64(a.chunk, L - off);
-      const Range pt = split_part(cur, a.wpc, w, A);
-      const int64_t e0 = ch.lo + off + pt.lo;
-      int b = r;
-      for (int j = 0; j < N; ++j) {
-        unit(pt.hi - pt.lo, j >= 1, j == 0, j <= N - 2, true, a.send[r] + e0 * E,
-             a.recv[r] + ((int64_t)b * a.count + e0) * E);
-        b = b == 0 ? N - 1 : b - 1;
-      }
-    }
-  }
-}
-
 struct Pipe {
   int r, c, w, pipe;
   FifoCtr* in_ctr;
@@ -473,9 +406,12 @@ __device__ __forceinline__ Pipe locate(const RingArgs& a) {
 // Bulk kernel
 // ---------------------------------------------------------------------------
 
-// Schedule iterator: the same walk as walk<>() (which the flag-packed kernel
-// uses), one FIFO slot step at a time, so that the bulk kernel can look one
-// step ahead. Empty units produce no step.
+// Schedule iterator: walks the ring schedule of one workgroup one FIFO slot
+// step at a time ("NCCL" book s. 2.3: a loop covers N chunks, stage j of rank
+// r visits chunk (r + N - 1 - j) mod N; all-gather round j moves block r - j,
+// "NCCL 专家课程 17", Bootstrap Ring 与 AllGather). Divisions happen once per
+// loop (or for a ragged tail chunk), never per stage: the chunk / block index
+// steps down by one each stage. Empty units produce no step.
 template <int DT, int MODE>
 struct StepIter {
   static constexpr int64_t E = sizeof(typename Elem<DT>::T);
@@ -558,14 +494,14 @@ struct StepIter {
     } while (m == 0);
   }
 
-  __device__ __forceinline__ void init(const RingArgs& a, int rank, int c, int part) {
+  __device__ __forceinline__ void init(const RingArgs& a, int rank, int c, int part, int64_t slice_elems) {
     N = a.nranks;
     r = rank;
     w = part;
     wpc = a.wpc;
     count = a.count;
     chunk = a.chunk;
-    slice = a.slot_bytes / E;
+    slice = slice_elems;
     send_r = a.send[r];
     recv_r = a.recv[r];
     const Range ch = channel_range(a.count, a.nchannels, c, A);
@@ -630,7 +566,7 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   uint32_t out_slot = (uint32_t)(out_base % nslots);
 
   StepIter<DT, MODE> it;
-  it.init(a, p.r, p.c, p.w);
+  it.init(a, p.r, p.c, p.w, a.slot_bytes / (int64_t)sizeof(T));
   StepIter<DT, MODE> nx = it;
   if (!nx.done) nx.next();
   const bool lds = a.lds_stage && a.vec_ok;
@@ -692,9 +628,10 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
 // Flag-packed kernel
 // ---------------------------------------------------------------------------
 
-// 16-byte line: {payload word 0, flag, payload word 1, flag}; each 8-byte
-// half is read as one 64-bit access, so a matching flag vouches for the word
-// stored with it.
+// Flag-packed FIFO line: 16 bytes {payload word 0, flag, payload word 1,
+// flag}; each 8-byte half is written and read as one 64-bit access, so a
+// matching flag vouches for the word stored with it. Polls until both flags
+// equal `flag` (or the wait is abandoned) and returns the two payload words.
 __device__ __forceinline__ u32x2 poll_line(const uint64_t* line, uint32_t flag, bool& stop, const WaitCtx& w) {
   uint64_t v0 = ld_relaxed(line);
   uint64_t v1 = ld_relaxed(line + 1);
@@ -762,47 +699,49 @@ __global__ void __launch_bounds__(kThreads) ring_flag_kernel(RingArgs a) {
   const uint64_t in_base = s_base[0];
   const uint64_t out_base = s_base[1];
   const uint64_t nslots = (uint64_t)a.nslots;
-  const int64_t slice = (a.slot_bytes / 2) / E;  // payload bytes per slot / element size
   uint64_t nrecv = 0, nsent = 0;
   uint64_t head_known = out_base;  // uniform across the workgroup
   uint64_t known_head = 0;         // thread 0
   bool stop = false;               // per thread: stop waiting
   const WaitCtx wc = wait_ctx(a);
+  uint32_t in_slot = (uint32_t)(in_base % nslots);
+  uint32_t out_slot = (uint32_t)(out_base % nslots);
 
-  walk<DT, MODE>(a, p.r, p.c, p.w,
-                 [&](int64_t m, bool recv, bool use_local, bool send, bool store, const char* local, char* out) {
-    for (int64_t s = 0; s < m; s += slice) {
-      const int64_t ns = min64(slice, m - s);
-      if (send && nsent + 1 > nslots) {
-        const uint64_t need = out_base + nsent + 1 - nslots;
-        if (head_known < need) {  // uniform branch
-          if (threadIdx.x == 0) {
-            if (!stop && known_head < need) {
-              known_head = wait_geq(&p.out_ctr->head, need, wc);
-              stop = known_head == 0;
-            }
-            s_head = known_head > need ? known_head : need;
+  StepIter<DT, MODE> it;
+  it.init(a, p.r, p.c, p.w, (a.slot_bytes / 2) / E);  // payload is half of a slot
+  for (; !it.done; it.next()) {
+    const bool recv = it.recv, send = it.send;
+    if (send && nsent + 1 > nslots) {
+      const uint64_t need = out_base + nsent + 1 - nslots;
+      if (head_known < need) {  // uniform branch
+        if (threadIdx.x == 0) {
+          if (!stop && known_head < need) {
+            known_head = wait_geq(&p.out_ctr->head, need, wc);
+            stop = known_head == 0;
           }
-          __syncthreads();
-          head_known = s_head;
-          __syncthreads();
+          s_head = known_head > need ? known_head : need;
         }
+        __syncthreads();
+        head_known = s_head;
+        __syncthreads();
       }
-      const uint32_t flag_in = (uint32_t)(in_base + nrecv + 1);
-      const uint32_t flag_out = (uint32_t)(out_base + nsent + 1);
-      const uint64_t* fin =
-          recv ? reinterpret_cast<const uint64_t*>(p.in_fifo + ((in_base + nrecv) % nslots) * a.slot_bytes) : nullptr;
-      uint64_t* fout =
-          send ? reinterpret_cast<uint64_t*>(p.out_fifo + ((out_base + nsent) % nslots) * a.slot_bytes) : nullptr;
-      const int64_t nbytes = ns * E;
-      const int64_t nlines = div_up(nbytes, 8);
-      const char* lp = use_local ? local + s * E : nullptr;
-      char* op = store ? out + s * E : nullptr;
-      for (int64_t li = threadIdx.x; li < nlines; li += kThreads) {
-        const int64_t bo = li * 8;
-        const int valid = (int)min64(8, nbytes - bo);
+    }
+    const uint32_t flag_in = (uint32_t)(in_base + nrecv + 1);
+    const uint32_t flag_out = (uint32_t)(out_base + nsent + 1);
+    const uint64_t* fin = recv ? reinterpret_cast<const uint64_t*>(p.in_fifo + (int64_t)in_slot * a.slot_bytes) : nullptr;
+    uint64_t* fout = send ? reinterpret_cast<uint64_t*>(p.out_fifo + (int64_t)out_slot * a.slot_bytes) : nullptr;
+    const int64_t nbytes = it.ns() * E;
+    const int nlines = (int)div_up(nbytes, 8);  // <= kThreads * kFlagLinesPerThread
+    const char* lp = it.use_local ? it.local() : nullptr;
+    char* op = it.store ? it.out() : nullptr;
+    if (nlines <= kThreads) {
+      // At most one line per thread (small messages): the shortest path from
+      // a flag's arrival to the next hop's store.
+      const int li = threadIdx.x;
+      if (li < nlines) {
+        const int valid = (int)min64(8, nbytes - (int64_t)li * 8);
         u32x2 loc = u32x2{0u, 0u};
-        if (lp) loc = load_payload<DT>(lp + bo, valid, a.vec_ok);
+        if (lp) loc = load_payload<DT>(lp + (int64_t)li * 8, valid, a.vec_ok);
         u32x2 x;
         if (fin) {
           x = poll_line(fin + 2 * li, flag_in, stop, wc);
@@ -814,16 +753,92 @@ __global__ void __launch_bounds__(kThreads) ring_flag_kernel(RingArgs a) {
           st_relaxed(fout + 2 * li, ((uint64_t)flag_out << 32) | x.x);
           st_relaxed(fout + 2 * li + 1, ((uint64_t)flag_out << 32) | x.y);
         }
-        if (op) store_payload<DT>(op + bo, x, valid, a.vec_ok);
+        if (op) store_payload<DT>(op + (int64_t)li * 8, x, valid, a.vec_ok);
       }
-      nrecv += recv ? 1 : 0;
-      nsent += send ? 1 : 0;
-      if (recv && nrecv % kFlagHeadEvery == 0) {  // uniform: release drained slots
+    } else {
+      // Several lines per thread: each thread owns lines tid, tid + 256, ...;
+      // all of its own-operand loads and first flag polls are issued together,
+      // then only lines whose flags have not arrived are polled again.
+      u32x2 x[kFlagLinesPerThread];
+      u32x2 loc[kFlagLinesPerThread];
+#pragma unroll
+      for (int u = 0; u < kFlagLinesPerThread; ++u) {
+        const int li = threadIdx.x + u * kThreads;
+        loc[u] = u32x2{0u, 0u};
+        if (lp && li < nlines) loc[u] = load_payload<DT>(lp + li * 8, (int)min64(8, nbytes - li * 8), a.vec_ok);
+      }
+      if (fin) {
+        uint64_t v0[kFlagLinesPerThread], v1[kFlagLinesPerThread];
+#pragma unroll
+        for (int u = 0; u < kFlagLinesPerThread; ++u) {
+          const int li = threadIdx.x + u * kThreads;
+          v0[u] = v1[u] = 0;
+          if (li < nlines) {
+            v0[u] = ld_relaxed(fin + 2 * li);
+            v1[u] = ld_relaxed(fin + 2 * li + 1);
+          }
+        }
+        uint32_t pending = 0;
+#pragma unroll
+        for (int u = 0; u < kFlagLinesPerThread; ++u) {
+          const int li = threadIdx.x + u * kThreads;
+          if (li < nlines && ((uint32_t)(v0[u] >> 32) != flag_in || (uint32_t)(v1[u] >> 32) != flag_in))
+            pending |= 1u << u;
+        }
+        if (pending && !stop) {
+          const uint64_t t0 = wall_clock64();
+          uint32_t spins = 0;
+          while (pending) {
+            if (give_up(wc, t0, ++spins)) {
+              stop = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int u = 0; u < kFlagLinesPerThread; ++u) {
+              if (pending & (1u << u)) {
+                const int li = threadIdx.x + u * kThreads;
+                v0[u] = ld_relaxed(fin + 2 * li);
+                v1[u] = ld_relaxed(fin + 2 * li + 1);
+                if ((uint32_t)(v0[u] >> 32) == flag_in && (uint32_t)(v1[u] >> 32) == flag_in) pending &= ~(1u << u);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kFlagLinesPerThread; ++u) {
+          x[u] = u32x2{(uint32_t)v0[u], (uint32_t)v1[u]};
+          if (lp) x[u] = VOp<DT, OP>::v2(x[u], loc[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kFlagLinesPerThread; ++u) x[u] = loc[u];
+      }
+#pragma unroll
+      for (int u = 0; u < kFlagLinesPerThread; ++u) {
+        const int li = threadIdx.x + u * kThreads;
+        if (li < nlines) {
+          if (fout) {
+            st_relaxed(fout + 2 * li, ((uint64_t)flag_out << 32) | x[u].x);
+            st_relaxed(fout + 2 * li + 1, ((uint64_t)flag_out << 32) | x[u].y);
+          }
+          if (op) store_payload<DT>(op + li * 8, x[u], (int)min64(8, nbytes - li * 8), a.vec_ok);
+        }
+      }
+    }
+    if (recv) {
+      ++nrecv;
+      in_slot = in_slot + 1 == (uint32_t)nslots ? 0 : in_slot + 1;
+      if (nrecv % kFlagHeadEvery == 0) {  // uniform: release drained slots
         __syncthreads();
         if (threadIdx.x == 0) st_relaxed(&p.in_ctr->head, in_base + nrecv);
       }
     }
-  });
+    if (send) {
+      ++nsent;
+      out_slot = out_slot + 1 == (uint32_t)nslots ? 0 : out_slot + 1;
+    }
+  }
   // Leave both counters at the number of steps this call moved, so the next
   // call (either protocol) starts from the same base on both sides.
   __syncthreads();

@@ -115,4 +115,39 @@ def test_config_defaults(L):
     assert cfg.chunk_bytes == 524_288
     assert cfg.nslots == 8
     assert cfg.slot_bytes == 32_768
-    assert cfg.flag_threshold_bytes == 65_536
+    assert cfg.flag_threshold_bytes == 0  # 0: AUTO uses the cost model
+
+
+def test_cost_model_shape(L):
+    """The model behind AUTO: flag-packed wins for tiny messages and bulk for
+    large ones, each protocol's time grows with size and with the hop count
+    2(N-1), and the flag protocol's bandwidth term carries twice the FIFO
+    bytes (the pages' LL factor)."""
+    for n, c in ((4, 4), (8, 8), (16, 16)):
+        tiny = rs.debug_model("allreduce", n, c, 8)
+        big = rs.debug_model("allreduce", n, c, 256 << 20)
+        assert tiny["flag_us"] < tiny["bulk_us"]
+        assert big["bulk_us"] < big["flag_us"]
+        prev = None
+        for k in range(3, 29):
+            m = rs.debug_model("allreduce", n, c, 1 << k)
+            if prev:
+                assert m["bulk_us"] >= prev["bulk_us"] and m["flag_us"] >= prev["flag_us"]
+            prev = m
+    # more ranks: more hops, higher latency floor
+    assert rs.debug_model("allreduce", 16, 16, 8)["flag_us"] > rs.debug_model("allreduce", 8, 16, 8)["flag_us"]
+    # reduce-scatter has half the hops of the all-reduce
+    ar = rs.debug_model("allreduce", 8, 8, 8)
+    rsm = rs.debug_model("reduce_scatter", 8, 8, 8)
+    assert rsm["bulk_us"] < ar["bulk_us"]
+    # crossover moves to larger messages as ranks and channels grow (measured on MI355X:
+    # ~64 KiB at 4x4, ~300 KiB at 8x8, ~1 MiB at 16x16)
+    def crossover(n, c):
+        for k in range(3, 30):
+            m = rs.debug_model("allreduce", n, c, 1 << k)
+            if m["bulk_us"] <= m["flag_us"]:
+                return 1 << k
+        return 1 << 30
+    x4, x8, x16 = crossover(4, 4), crossover(8, 8), crossover(16, 16)
+    assert x4 < x8 < x16
+    assert (16 << 10) <= x4 <= (256 << 10) and (128 << 10) <= x8 <= (1 << 20) and (512 << 10) <= x16 <= (4 << 20)
