@@ -256,3 +256,28 @@ def test_allreduce_random_bit_patterns(proto, dtype):
         got = _run_allreduce(xs, dtype, op, nch, proto, chunk_bytes=16384)
         want = oracle.ring_allreduce(xs, op, dtype, nchannels=nch, chunk_bytes=16384)
         _assert_same(got, want, dtype, f"{dtype} {op} exponents {lo}..{hi}")
+
+
+@pytest.mark.parametrize("n,nch", [(16, 16), (8, 8), (4, 4)])
+def test_auto_protocol_choice_does_not_change_results(n, nch):
+    """Around the cost model's crossover AUTO switches between protocols; the
+    flag protocol's smaller chunk must not change the partition there, so the
+    bits equal the oracle's with the default 512 KiB chunk either way."""
+    comm = rs.comm_init(n, nch, "auto")
+    seen = set()
+    try:
+        for k, nbytes in enumerate((16 << 10, 64 << 10, 256 << 10, 512 << 10, 1 << 20, 2 << 20)):
+            count = nbytes // 4 + 3  # ragged tail
+            xs = _inputs(n, count, "float32", 1000 + k)
+            G.say(f"auto N={n} C={nch} bytes/rank={nbytes}")
+            send = [G.to_device(x, "float32") for x in xs]
+            recv = [G.empty_like_rank(count, "float32") for _ in range(n)]
+            rs.allreduce(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            seen.add(rs.comm_query(comm)["last_proto"])
+            want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=nch, chunk_bytes=524_288)
+            _assert_same([G.to_host(t, "float32") for t in recv], want, "float32", f"auto {nbytes} B/rank")
+    finally:
+        rs.comm_destroy(comm)
+    assert seen == {1, 2}, f"expected both protocols across the sizes, saw {seen}"
