@@ -90,15 +90,17 @@ def test_workload3_ddp_buckets_back_to_back():
 @pytest.mark.parametrize("op", ["sum", "max"])
 def test_workload4_size_sweep(op):
     """16 ranks, int32 in [-2^20, 2^20], 8 B .. 256 MiB per rank; flag-packed
-    below 64 KiB, bulk above, 16 channels."""
+    below 64 KiB, bulk above (the sweep's own fixed threshold, not the cost
+    model), 16 channels."""
     import torch
 
     n, nch = 16, 16
-    comm = rs.comm_init(n, nch, "auto")
+    comm = rs.comm_init(n, nch, "auto", flag_threshold_bytes=65536)
     try:
         for k, size in enumerate(synth.WORKLOADS[4]["sizes_bytes"]):
             count = size // 4
-            G.say(f"sweep op={op} bytes/rank={size} proto={'flag' if size < 65536 else 'bulk'}")
+            want_proto = 2 if size < 65536 else 1
+            G.say(f"sweep op={op} bytes/rank={size} proto={'flag' if want_proto == 2 else 'bulk'}")
             if size <= (4 << 20):
                 xs = synth.rank_inputs(4, n, count, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
                 send = [G.to_device(x, "int32") for x in xs]
@@ -109,6 +111,7 @@ def test_workload4_size_sweep(op):
             rs.allreduce(comm, send, recv, op=op)
             G.sync()
             G.check_comm_ok(comm)
+            assert rs.comm_query(comm)["last_proto"] == want_proto, f"size {size}"
             assert _all_ranks_equal(recv), f"size {size}: ranks disagree"
             if xs is not None:
                 want = oracle.ring_allreduce(xs, op, "int32", nchannels=nch)
