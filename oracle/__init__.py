@@ -1,8 +1,9 @@
-"""CPU oracle for the ring collectives (test infrastructure only).
+"""CPU oracle for the ring collectives and the double-binary-tree
+all-reduce (test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
-``bench.py`` may import this package. See ``oracle/ring.py`` for the sources
-it follows and the readings it takes.
+``bench.py`` may import this package. See ``oracle/ring.py`` and
+``oracle/tree.py`` for the sources they follow and the readings they take.
 """
 from .ring import (  # noqa: F401
     DTYPES,
@@ -28,3 +29,4 @@ from .ring import (  # noqa: F401
     ring_allreduce,
     ring_reduce_scatter,
 )
+from .tree import btree, dtree, tree_allreduce, tree_root, tree_split  # noqa: F401,E402
