@@ -104,6 +104,25 @@ typedef enum {
   RINGSIM_PROTO_FLAG = 2
 } ringsim_proto_t;
 
+/* All-reduce algorithms. RING is the ring schedule above. TREE is the double
+ * binary tree ("NCCL" book, ch. 4, ncclGetBtree / ncclGetDtree; ch. 5,
+ * tree.cc: all-reduce only): two binary trees over the ranks, the second the
+ * mirror (even N) or the shift by one rank (odd N) of the first, each
+ * reducing one half of the buffer up to its root and broadcasting the result
+ * back down. Tree 1 takes elements [h, count) with
+ * h = min(count, alignUp(ceil(count/2), 16/elemsize)); a rank folds its own
+ * data, then its first child's partial, then its second child's. The tree
+ * always moves flag-packed lines and needs 2*log2(N) dependent hops instead
+ * of the ring's 2(N-1). AUTO takes the tree only where the fold order cannot
+ * change a result bit (integer types, and max/min of any type) and the cost
+ * model predicts it faster; with proto = BULK it always takes the ring. The
+ * algorithm applies to ringsim_allreduce only. */
+typedef enum {
+  RINGSIM_ALGO_AUTO = 0,
+  RINGSIM_ALGO_RING = 1,
+  RINGSIM_ALGO_TREE = 2
+} ringsim_algo_t;
+
 typedef enum {
   RINGSIM_COLL_ALLREDUCE = 0,
   RINGSIM_COLL_REDUCE_SCATTER = 1,
@@ -119,6 +138,7 @@ typedef struct {
   int nslots;                  /* bulk FIFO depth; default 8 (NCCL_STEPS) */
   int timeout_ms;              /* bound on any single wait; default 10000, env RINGSIM_TIMEOUT_MS */
   size_t flag_threshold_bytes; /* AUTO: FLAG below this many bytes per rank; default 0 = cost model */
+  int algo;                    /* ringsim_algo_t for all-reduces; default AUTO, env RINGSIM_ALGO=ring|tree|auto */
 } ringsim_config_t;
 
 /* Read-only description of a communicator. */
@@ -138,11 +158,15 @@ typedef struct {
   int compute_units;
   uint64_t calls;              /* collective calls enqueued so far */
   int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG, 0 if none */
+  int algo;                    /* configured all-reduce algorithm (ringsim_algo_t) */
+  int tree_channels;           /* most channels per tree an all-reduce may use */
+  size_t tree_fifo_bytes;      /* double-tree FIFO bytes in HBM */
+  int last_algo;               /* algorithm of the latest all-reduce: RINGSIM_ALGO_RING/TREE, 0 if none */
 } ringsim_comm_info_t;
 
 /* Fills *cfg with the defaults. Environment overrides, read by this call:
  * RINGSIM_CHUNK_BYTES, RINGSIM_WPC, RINGSIM_SLOT_BYTES, RINGSIM_NSLOTS,
- * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD; RINGSIM_DEBUG=WARN|INFO logs to
+ * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD, RINGSIM_ALGO; RINGSIM_DEBUG=WARN|INFO logs to
  * stderr. Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
  * the workgroups of simulated rank r return at once, so that the bounded
  * waits of its neighbours expire and the failure path can be exercised. */
@@ -217,6 +241,17 @@ const char* ringsim_get_error_string(ringsim_result_t result);
  * all-gather output) on each protocol. Touches no device. */
 ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t bytes_per_rank, double* us_bulk,
                                      double* us_flag);
+
+/* Host-only tree shape. Writes links[6] = (parent, first child, second
+ * child) of `rank` in tree 0, then the same in tree 1 (-1 = none), for a
+ * double binary tree over `nranks` ranks ("NCCL" book, ch. 4). */
+ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
+
+/* Host-only cost model of the tree all-reduce with `tree_channels` channels
+ * per tree and `bytes_per_rank` bytes per rank: base + 2 x tree depth x the
+ * flag protocol's hop latency + the flag protocol's bytes over the bandwidth
+ * of the workgroups that move them. Writes the predicted microseconds. */
+ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us);
 
 /* Host-only view of the partition used by the kernels. For `coll`
  * (ringsim_coll_t), writes rows of 5 int64 values

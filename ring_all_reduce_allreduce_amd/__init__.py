@@ -13,6 +13,8 @@ Functions carry the C names without the ``ringsim_`` prefix:
     alltoall(comm, sendbufs, recvbufs, count=None, stream=None)
     get_async_error(comm); abort(comm); comm_query(comm); comm_destroy(comm)
     debug_plan(coll, count, nranks, nchannels, chunk_bytes, dtype)
+    debug_model(coll, nranks, nchannels, bytes_per_rank)
+    debug_tree(nranks, rank); debug_tree_model(nranks, tree_channels, bytes_per_rank)
 
 ``sendbufs``/``recvbufs`` are lists (one per simulated rank) of CUDA/HIP
 tensors of one dtype, or of raw device addresses (ints; then ``dtype`` and the
@@ -48,6 +50,7 @@ DTYPES = {"int32": 0, "int64": 1, "float32": 2, "bfloat16": 3}
 ELEM_SIZE = {"int32": 4, "int64": 8, "float32": 4, "bfloat16": 2}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 PROTOS = {"auto": 0, "bulk": 1, "flag": 2}
+ALGOS = {"auto": 0, "ring": 1, "tree": 2}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "alltoall": 3}
 
 
@@ -66,6 +69,7 @@ class Config(ctypes.Structure):
         ("nslots", ctypes.c_int),
         ("timeout_ms", ctypes.c_int),
         ("flag_threshold_bytes", ctypes.c_size_t),
+        ("algo", ctypes.c_int),
     ]
 
 
@@ -86,6 +90,10 @@ class CommInfo(ctypes.Structure):
         ("compute_units", ctypes.c_int),
         ("calls", ctypes.c_uint64),
         ("last_proto", ctypes.c_int),
+        ("algo", ctypes.c_int),
+        ("tree_channels", ctypes.c_int),
+        ("tree_fifo_bytes", ctypes.c_size_t),
+        ("last_algo", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:
@@ -122,6 +130,8 @@ def lib() -> ctypes.CDLL:
         "ringsim_get_error_string": (ctypes.c_char_p, [res]),
         "ringsim_debug_plan": (res, [i, sz, i, i, sz, i, ctypes.POINTER(ctypes.c_int64), sz, ctypes.POINTER(sz)]),
         "ringsim_debug_model": (res, [i, i, i, sz, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+        "ringsim_debug_tree": (res, [i, i, ctypes.POINTER(ctypes.c_int)]),
+        "ringsim_debug_tree_model": (res, [i, i, sz, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (rt, args) in sig.items():
         f = getattr(L, name)
@@ -168,8 +178,11 @@ def config_default() -> Config:
 def comm_init(nranks: int, nchannels: int, proto: str | int = "auto", **config) -> Comm:
     """Creates a communicator. Keyword tunables: chunk_bytes,
     workgroups_per_channel, slot_bytes, nslots, timeout_ms,
-    flag_threshold_bytes (0 or absent = library default)."""
+    flag_threshold_bytes, algo ("auto", "ring", "tree"; 0 or absent = library
+    default)."""
     p = PROTOS[proto] if isinstance(proto, str) else int(proto)
+    if isinstance(config.get("algo"), str):
+        config["algo"] = ALGOS[config["algo"]]
     h = ctypes.c_void_p()
     if config:
         cfg = Config()
@@ -288,6 +301,23 @@ def debug_model(coll: str | int, nranks: int, nchannels: int, bytes_per_rank: in
     _check(lib().ringsim_debug_model(c, nranks, nchannels, bytes_per_rank, ctypes.byref(b), ctypes.byref(f)),
            "ringsim_debug_model")
     return {"bulk_us": b.value, "flag_us": f.value}
+
+
+def debug_tree(nranks: int, rank: int) -> tuple[tuple[int, int, int], tuple[int, int, int]]:
+    """((parent, child0, child1) in tree 0, the same in tree 1) of ``rank``;
+    host-only."""
+    out = (ctypes.c_int * 6)()
+    _check(lib().ringsim_debug_tree(nranks, rank, out), "ringsim_debug_tree")
+    v = list(out)
+    return tuple(v[:3]), tuple(v[3:])
+
+
+def debug_tree_model(nranks: int, tree_channels: int, bytes_per_rank: int) -> float:
+    """Predicted microseconds of a tree all-reduce; host-only."""
+    us = ctypes.c_double()
+    _check(lib().ringsim_debug_tree_model(nranks, tree_channels, bytes_per_rank, ctypes.byref(us)),
+           "ringsim_debug_tree_model")
+    return us.value
 
 
 def debug_plan(coll: str | int, count: int, nranks: int, nchannels: int, chunk_bytes: int, dtype: str | int):

@@ -50,4 +50,15 @@ inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, 
   return m.base_us + hops * (flag ? m.hop_us_flag : m.hop_us_bulk) + bytes / (gbs * 1e3);
 }
 
+// Predicted microseconds of a double-binary-tree all-reduce: the reduce
+// climbs `depth` hops to each root and the broadcast descends as many, all
+// in flag-packed lines; the flag protocol's bytes move through the 4 x N x
+// tree_channels workgroups (two trees, an up and a down role each).
+inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double bytes_per_rank) {
+  if (nranks <= 1) return m.base_us;
+  const double bytes = model_bytes(kModelAllReduce, nranks, bytes_per_rank, true);
+  const double gbs = std::min(m.flag_max_gbs, m.flag_wg_gbs * 4.0 * nranks * tree_channels);
+  return m.base_us + 2.0 * depth * m.hop_us_flag + bytes / (gbs * 1e3);
+}
+
 }  // namespace ringsim

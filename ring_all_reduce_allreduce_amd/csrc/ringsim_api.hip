@@ -19,6 +19,7 @@
 #include <unordered_set>
 
 #include "ring_model.h"
+#include "tree_plan.h"
 #include "ring_plan.h"
 #include "ringsim_internal.h"
 
@@ -61,6 +62,16 @@ long env_long(const char* name, long dflt) {
   return (end && *end == 0) ? v : dflt;
 }
 
+// RINGSIM_ALGO: "ring", "tree", "auto" or the enum value.
+int env_algo(int dflt) {
+  const char* e = std::getenv("RINGSIM_ALGO");
+  if (!e || !*e) return dflt;
+  if (!std::strcmp(e, "ring")) return RINGSIM_ALGO_RING;
+  if (!std::strcmp(e, "tree")) return RINGSIM_ALGO_TREE;
+  if (!std::strcmp(e, "auto")) return RINGSIM_ALGO_AUTO;
+  return (int)env_long("RINGSIM_ALGO", dflt);
+}
+
 }  // namespace
 
 struct ringsim_comm {
@@ -91,6 +102,15 @@ struct ringsim_comm {
   uint32_t* host_words_dev;  // the same words as the device sees them
   uint64_t calls;
   int last_proto;
+  int algo;                // configured all-reduce algorithm
+  int last_algo;
+  int tree_channels;       // channels per tree in the tree FIFO arrays
+  int tree_depth;          // deeper of the two trees (edges from root to leaf)
+  int8_t tree_link[2][RINGSIM_MAX_RANKS][3];
+  char* tree_fifo;
+  size_t tree_fifo_bytes;
+  FifoCtr* tree_ctr;
+  size_t tree_ctr_bytes;
   ringsim_result_t sticky;
   hipStream_t last_stream;
   bool has_last_stream;
@@ -223,6 +243,67 @@ ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void*
   return RINGSIM_SUCCESS;
 }
 
+// Tree channels for one all-reduce: enough that each workgroup moves at
+// least kTreeChannelBytes of the half buffer its tree owns.
+constexpr size_t kTreeChannelBytes = 16384;
+
+int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank) {
+  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), (int64_t)kTreeChannelBytes);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, c->tree_channels));
+}
+
+// Predicted time of the ring as AUTO would run it.
+double ring_auto_us(const ringsim_comm* c, size_t bytes_per_rank) {
+  const RingModel m;
+  const bool flag = c->proto == RINGSIM_PROTO_FLAG ||
+                    (c->proto == RINGSIM_PROTO_AUTO && auto_picks_flag(c, kAllReduce, bytes_per_rank));
+  return model_us(m, kAllReduce, c->nranks, c->nchannels, (double)bytes_per_rank, flag);
+}
+
+// AUTO's algorithm: the tree only where the fold order cannot show in the
+// result (integers wrap associatively; max/min pick one input), only when
+// the flag-packed lines it moves are allowed, and only when it is predicted
+// to be faster than the ring.
+bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t bytes_per_rank) {
+  const bool order_free = dtype == RINGSIM_INT32 || dtype == RINGSIM_INT64 || op == RINGSIM_MAX || op == RINGSIM_MIN;
+  if (!order_free || c->proto == RINGSIM_PROTO_BULK || c->tree_channels < 1) return false;
+  const RingModel m;
+  return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank), (double)bytes_per_rank) <
+         ring_auto_us(c, bytes_per_rank);
+}
+
+ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const* rb, size_t count, int dtype,
+                             int op, bool vec, hipStream_t s) {
+  TreeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < c->nranks; ++r) {
+    a.send[r] = static_cast<const char*>(sb[r]);
+    a.recv[r] = static_cast<char*>(rb[r]);
+  }
+  a.count = (int64_t)count;
+  a.nranks = c->nranks;
+  a.nchannels = tree_channels_for(c, count * (size_t)dtype_size(dtype));
+  a.ch_stride = c->tree_channels;
+  a.nslots = kTreeSlots;
+  a.slot_bytes = kTreeSlotBytes;
+  a.head_every = kTreeSlots / 2;
+  a.vec_ok = vec;
+  a.skip_rank = c->skip_rank;
+  std::memcpy(a.link, c->tree_link, sizeof(a.link));
+  a.fifo = c->tree_fifo;
+  a.ctr = c->tree_ctr;
+  a.dev_abort = c->dev_abort;
+  a.host_abort = c->host_words_dev;
+  a.host_err = c->host_words_dev + 1;
+  a.timeout_ticks = c->timeout_ticks;
+  const hipError_t e = launch_tree_flag(a, dtype, op, s);
+  if (e != hipSuccess) {
+    RS_LOG(kLogWarn, "tree kernel launch failed: %s", hipGetErrorString(e));
+    return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  }
+  return RINGSIM_SUCCESS;
+}
+
 ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
                           int dtype, int op, ringsim_stream_t stream) {
   ringsim_result_t res = check_comm(c);
@@ -244,10 +325,16 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
     // A single rank is a local copy ("NCCL" book, enqueue chapter, taskAppend).
     return launch_local_copy(c, sb, rb, count * esize, s);
   }
+  const size_t per_rank_bytes = (mode == kAllReduce ? count : count * n) * esize;
+  if (mode == kAllReduce) {
+    const bool tree = c->algo == RINGSIM_ALGO_TREE ||
+                      (c->algo == RINGSIM_ALGO_AUTO && auto_picks_tree(c, dtype, op, per_rank_bytes));
+    c->last_algo = tree ? RINGSIM_ALGO_TREE : RINGSIM_ALGO_RING;
+    if (tree) return launch_tree(c, sb, rb, count, dtype, op, vec, s);
+  }
   RingArgs a;
   fill_common(c, &a, sb, rb);
   a.count = (int64_t)count;
-  const size_t per_rank_bytes = (mode == kAllReduce ? count : count * n) * esize;
   bool flag = false;
   fill_proto(c, &a, mode, per_rank_bytes, esize, &flag);
   // Vector moves need every unit to start on a 16-byte boundary; for the
@@ -266,6 +353,10 @@ void free_comm_memory(ringsim_comm* c) {
   if (c->fifo) (void)hipFree(c->fifo);
   if (c->flag_fifo) (void)hipFree(c->flag_fifo);
   if (c->ctr) (void)hipFree(c->ctr);
+  if (c->tree_fifo) (void)hipFree(c->tree_fifo);
+  if (c->tree_ctr) (void)hipFree(c->tree_ctr);
+  c->tree_fifo = nullptr;
+  c->tree_ctr = nullptr;
   if (c->dev_abort) (void)hipFree(c->dev_abort);
   if (c->host_words) (void)hipHostFree(c->host_words);
   c->fifo = c->flag_fifo = nullptr;
@@ -287,6 +378,7 @@ ringsim_result_t ringsim_config_default(ringsim_config_t* cfg) {
   cfg->nslots = (int)env_long("RINGSIM_NSLOTS", kDefaultSlots);
   cfg->timeout_ms = (int)env_long("RINGSIM_TIMEOUT_MS", 10000);
   cfg->flag_threshold_bytes = (size_t)env_long("RINGSIM_FLAG_THRESHOLD", 0);
+  cfg->algo = env_algo(RINGSIM_ALGO_AUTO);
   return RINGSIM_SUCCESS;
 }
 
@@ -309,7 +401,9 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
     if (user_cfg->nslots) cfg.nslots = user_cfg->nslots;
     if (user_cfg->timeout_ms) cfg.timeout_ms = user_cfg->timeout_ms;
     if (user_cfg->flag_threshold_bytes) cfg.flag_threshold_bytes = user_cfg->flag_threshold_bytes;
+    if (user_cfg->algo) cfg.algo = user_cfg->algo;
   }
+  if (cfg.algo < RINGSIM_ALGO_AUTO || cfg.algo > RINGSIM_ALGO_TREE) return RINGSIM_INVALID_ARGUMENT;
   if (cfg.chunk_bytes == 0 || cfg.chunk_bytes % 16 || cfg.chunk_bytes > ((size_t)1 << 30))
     return RINGSIM_INVALID_ARGUMENT;
   if (cfg.slot_bytes < 4096 || cfg.slot_bytes % 4096 || cfg.slot_bytes > ((size_t)1 << 22))
@@ -352,6 +446,13 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   const int slices = (int)div_up((int64_t)stage_bytes, (int64_t)cfg.slot_bytes);
   const int nslots = std::max(cfg.nslots, 2 * slices);
 
+  // Tree channels: every workgroup of a tree launch (4 per rank and channel)
+  // must be resident at once, like the ring's.
+  const int tree_per_cu = tree_blocks_per_cu();
+  const int64_t tree_resident = (int64_t)tree_per_cu * cus;
+  const int tree_channels = nranks < 2 ? 0 : (int)std::min<int64_t>(nchannels, tree_resident / (4 * (int64_t)nranks));
+  if (cfg.algo == RINGSIM_ALGO_TREE && nranks > 1 && tree_channels < 1) return RINGSIM_INVALID_USAGE;
+
   ringsim_comm* c = new (std::nothrow) ringsim_comm();
   if (!c) return RINGSIM_SYSTEM_ERROR;
   std::memset(c, 0, sizeof(*c));
@@ -373,17 +474,37 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->compute_units = cus;
   c->blocks_per_cu = per_cu;
   c->sticky = RINGSIM_SUCCESS;
+  c->algo = cfg.algo;
+  c->tree_channels = tree_channels;
+  c->tree_depth = double_tree_depth(nranks);
+  for (int t = 0; t < 2; ++t) {
+    for (int r = 0; r < nranks; ++r) {
+      const TreeLinks l = double_tree(nranks, r, t);
+      c->tree_link[t][r][0] = (int8_t)l.parent;
+      c->tree_link[t][r][1] = (int8_t)l.kid[0];
+      c->tree_link[t][r][2] = (int8_t)l.kid[1];
+    }
+  }
 
   const int64_t pipes = nc * wpc;
   c->fifo_bytes = (size_t)pipes * nslots * cfg.slot_bytes;
   c->flag_fifo_bytes = (size_t)nc * kFlagSlots * kFlagSlotBytes;
   c->ctr_bytes = (size_t)pipes * sizeof(FifoCtr);
+  const size_t tree_fifos = (size_t)2 * tree_channels * nranks * 2;
+  c->tree_fifo_bytes = tree_fifos * kTreeSlots * kTreeSlotBytes;
+  c->tree_ctr_bytes = tree_fifos * sizeof(FifoCtr);
   bool ok = hipMalloc((void**)&c->fifo, c->fifo_bytes) == hipSuccess &&
             hipMalloc((void**)&c->flag_fifo, c->flag_fifo_bytes) == hipSuccess &&
             hipMalloc((void**)&c->ctr, c->ctr_bytes) == hipSuccess &&
             hipMalloc((void**)&c->dev_abort, 256) == hipSuccess &&
             hipHostMalloc((void**)&c->host_words, 256, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   if (ok) ok = hipHostGetDevicePointer((void**)&c->host_words_dev, c->host_words, 0) == hipSuccess;
+  if (ok && tree_fifos) {
+    ok = hipMalloc((void**)&c->tree_fifo, c->tree_fifo_bytes) == hipSuccess &&
+         hipMalloc((void**)&c->tree_ctr, c->tree_ctr_bytes) == hipSuccess &&
+         hipMemset(c->tree_fifo, 0, c->tree_fifo_bytes) == hipSuccess &&
+         hipMemset(c->tree_ctr, 0, c->tree_ctr_bytes) == hipSuccess;
+  }
   // Flags of the flag-packed FIFO start at zero, a value no step ever uses.
   if (ok) ok = hipMemset(c->flag_fifo, 0, c->flag_fifo_bytes) == hipSuccess &&
                hipMemset(c->ctr, 0, c->ctr_bytes) == hipSuccess && hipMemset(c->dev_abort, 0, 256) == hipSuccess &&
@@ -447,6 +568,10 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
   info->compute_units = comm->compute_units;
   info->calls = comm->calls;
   info->last_proto = comm->last_proto;
+  info->algo = comm->algo;
+  info->tree_channels = comm->tree_channels;
+  info->tree_fifo_bytes = comm->tree_fifo_bytes;
+  info->last_algo = comm->last_algo;
   return RINGSIM_SUCCESS;
 }
 
@@ -548,6 +673,26 @@ ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t
   const RingModel m;
   *us_bulk = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, false);
   *us_flag = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, true);
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links) {
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || rank < 0 || rank >= nranks || !links)
+    return RINGSIM_INVALID_ARGUMENT;
+  for (int t = 0; t < 2; ++t) {
+    const TreeLinks l = double_tree(nranks, rank, t);
+    links[3 * t] = l.parent;
+    links[3 * t + 1] = l.kid[0];
+    links[3 * t + 2] = l.kid[1];
+  }
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us) {
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || tree_channels < 1 || tree_channels > RINGSIM_MAX_CHANNELS || !us)
+    return RINGSIM_INVALID_ARGUMENT;
+  const RingModel m;
+  *us = tree_model_us(m, nranks, double_tree_depth(nranks), tree_channels, (double)bytes_per_rank);
   return RINGSIM_SUCCESS;
 }
 

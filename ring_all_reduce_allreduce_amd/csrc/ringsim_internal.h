@@ -62,6 +62,35 @@ struct RingArgs {
   int lds_stage;        // bulk: stage each step's own operand in LDS (2 x slot_bytes dynamic LDS)
 };
 
+// Double-binary-tree all-reduce (flag-packed lines). Workgroup b of the grid
+// is (rank, tree, channel, role) with b = ((rank * 2 + tree) * nchannels +
+// channel) * 2 + role; role 0 reduces up the tree, role 1 broadcasts down.
+// FIFO f = ((tree * ch_stride + channel) * nranks + node) * 2 + dir carries
+// node -> parent (dir 0, "up") or parent -> node (dir 1, "down").
+struct TreeArgs {
+  const char* send[RINGSIM_MAX_RANKS];
+  char* recv[RINGSIM_MAX_RANKS];
+  int64_t count;        // elements per rank
+  int nranks;
+  int nchannels;        // tree channels of this launch (<= ch_stride)
+  int ch_stride;        // tree channels in the FIFO and counter arrays
+  int nslots;
+  int slot_bytes;       // flag slot: half of it is payload
+  int head_every;       // consumers publish `head` every this many steps
+  int vec_ok;
+  int skip_rank;
+  int8_t link[2][RINGSIM_MAX_RANKS][3];  // per tree and rank: parent, first child, second child
+  char* fifo;           // [tree][channel][node][dir][slot][slot_bytes]
+  FifoCtr* ctr;         // [tree][channel][node][dir]
+  uint32_t* dev_abort;
+  const uint32_t* host_abort;
+  uint32_t* host_err;
+  uint64_t timeout_ticks;
+};
+
+constexpr int kTreeSlots = 8;
+constexpr int kTreeSlotBytes = kFlagSlotBytes;
+
 struct CopyArgs {
   const char* src[RINGSIM_MAX_RANKS];
   char* dst[RINGSIM_MAX_RANKS];
@@ -75,6 +104,9 @@ struct CopyArgs {
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_flag(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_tree_flag(const TreeArgs& a, int dtype, int op, hipStream_t s);
+// Max co-resident tree workgroups per CU over every dtype and op.
+int tree_blocks_per_cu();
 // Max co-resident workgroups per CU over every ring kernel instantiation, the
 // bulk kernels launched with `bulk_lds_bytes` of dynamic LDS.
 int ring_blocks_per_cu(size_t bulk_lds_bytes);

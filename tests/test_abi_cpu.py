@@ -151,3 +151,44 @@ def test_cost_model_shape(L):
     x4, x8, x16 = crossover(4, 4), crossover(8, 8), crossover(16, 16)
     assert x4 < x8 < x16
     assert (16 << 10) <= x4 <= (256 << 10) and (128 << 10) <= x8 <= (1 << 20) and (512 << 10) <= x16 <= (4 << 20)
+
+
+def test_library_tree_matches_oracle_tree(L):
+    """The kernels' tree links (built in C++ from the same page) equal the
+    oracle's for every rank count the library accepts."""
+    for n in range(1, 65):
+        for r in range(n):
+            assert rs.debug_tree(n, r) == oracle.dtree(n, r), (n, r)
+
+
+def test_tree_debug_arguments(L):
+    out = (ctypes.c_int * 6)()
+    assert L.ringsim_debug_tree(0, 0, out) == 4
+    assert L.ringsim_debug_tree(4, 4, out) == 4
+    assert L.ringsim_debug_tree(65, 0, out) == 4
+    assert L.ringsim_debug_tree(4, 0, None) == 4
+    us = ctypes.c_double()
+    assert L.ringsim_debug_tree_model(4, 0, 16, ctypes.byref(us)) == 4
+    assert L.ringsim_debug_tree_model(4, 1, 16, None) == 4
+    h = ctypes.c_void_p(12345)
+    cfg = rs.Config()
+    cfg.algo = 3
+    assert L.ringsim_comm_init_config(ctypes.byref(h), 4, 1, 0, ctypes.byref(cfg)) == 4
+    assert h.value == 12345
+
+
+def test_tree_config_default(L):
+    assert rs.config_default().algo == 0  # AUTO
+
+
+def test_tree_model_shape(L):
+    """2 log2(N) hops against the ring's 2(N-1): the tree is predicted faster
+    for tiny messages at 8 and 16 ranks, slower for large ones, and its
+    latency floor grows with the tree depth, not with N."""
+    for n, c in ((8, 8), (16, 16)):
+        ring = rs.debug_model("allreduce", n, c, 8)
+        assert rs.debug_tree_model(n, 1, 8) < min(ring["flag_us"], ring["bulk_us"])
+        big = rs.debug_model("allreduce", n, c, 256 << 20)
+        assert rs.debug_tree_model(n, c, 256 << 20) > big["bulk_us"]
+    assert rs.debug_tree_model(16, 1, 8) - rs.debug_tree_model(8, 1, 8) < \
+        rs.debug_model("allreduce", 16, 16, 8)["flag_us"] - rs.debug_model("allreduce", 8, 16, 8)["flag_us"]

@@ -91,11 +91,11 @@ def test_workload3_ddp_buckets_back_to_back():
 def test_workload4_size_sweep(op):
     """16 ranks, int32 in [-2^20, 2^20], 8 B .. 256 MiB per rank; flag-packed
     below 64 KiB, bulk above (the sweep's own fixed threshold, not the cost
-    model), 16 channels."""
+    model), 16 channels, ring algorithm."""
     import torch
 
     n, nch = 16, 16
-    comm = rs.comm_init(n, nch, "auto", flag_threshold_bytes=65536)
+    comm = rs.comm_init(n, nch, "auto", flag_threshold_bytes=65536, algo="ring")
     try:
         for k, size in enumerate(synth.WORKLOADS[4]["sizes_bytes"]):
             count = size // 4
