@@ -219,8 +219,8 @@ def copy_calibration(args) -> int:
 
 def size_sweep(args) -> int:
     """Latency / bandwidth of the int32 all-reduce across message sizes
-    (default 16 ranks, 16 channels); AUTO picks the protocol per size with the
-    library's cost model, and each line reports the protocol it ran."""
+    (default 16 ranks, 16 channels); AUTO picks the algorithm and protocol per
+    size with the library's cost model, and each line reports what it ran."""
     import numpy as np
     import torch
 
@@ -229,7 +229,7 @@ def size_sweep(args) -> int:
     import synth
 
     n, nch = args.sweep_ranks, args.sweep_channels
-    comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None)
+    comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo)
     size = 8
     k = 0
     while size <= args.sweep_max_bytes:
@@ -255,10 +255,12 @@ def size_sweep(args) -> int:
             ends[i].record()
         torch.cuda.synchronize()
         t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
-        proto = {1: "bulk", 2: "flag"}.get(rs.comm_query(comm)["last_proto"], "?")
+        info = rs.comm_query(comm)
+        algo = {1: "ring", 2: "tree"}.get(info["last_algo"], "?")
+        proto = "flag" if algo == "tree" else {1: "bulk", 2: "flag"}.get(info["last_proto"], "?")
         busbw = size / t * bus_factor("allreduce", n) / 1e9
         byts = algorithmic_bytes("allreduce", n, size)
-        print(json.dumps({"nranks": n, "nchannels": nch, "bytes_per_rank": size, "proto": proto,
+        print(json.dumps({"nranks": n, "nchannels": nch, "bytes_per_rank": size, "algo": algo, "proto": proto,
                           "us": round(t * 1e6, 2),
                           "busbw_gbs": round(busbw, 3), "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
                           "sampled_parity": ok}), flush=True)
@@ -289,6 +291,8 @@ def main() -> int:
     ap.add_argument("--sweep-ranks", type=int, default=16)
     ap.add_argument("--sweep-channels", type=int, default=16)
     ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "ring", "tree"],
+                    help="all-reduce algorithm for --sweep (auto: the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time the library's copy kernel on 1 GiB (a one-rank all-to-all) instead; used to "
                          "scale the HBM byte counters")
