@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "busBW GB/s of N-rank ring all-reduce on 1 MI355X; % of HBM peak"
 KERNEL_SOURCES = [
     os.path.join(ROOT, "ring_all_reduce_allreduce_amd", "csrc", f)
-    for f in ("ringsim_kernels.hip", "ring_plan.h", "ringsim_internal.h")
+    for f in ("ring_bulk.hip", "ringsim_device.h", "ring_plan.h", "ringsim_internal.h")
 ]
 
 # Named single-GPU workloads. "ar8x64" is the headline; the others exist for
@@ -257,7 +257,7 @@ def size_sweep(args) -> int:
         t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
         info = rs.comm_query(comm)
         algo = {1: "ring", 2: "tree"}.get(info["last_algo"], "?")
-        proto = "flag" if algo == "tree" else {1: "bulk", 2: "flag"}.get(info["last_proto"], "?")
+        proto = "flag" if algo == "tree" else {1: "bulk", 2: "flag", 3: "wide"}.get(info["last_proto"], "?")
         busbw = size / t * bus_factor("allreduce", n) / 1e9
         byts = algorithmic_bytes("allreduce", n, size)
         print(json.dumps({"nranks": n, "nchannels": nch, "bytes_per_rank": size, "algo": algo, "proto": proto,
@@ -290,7 +290,7 @@ def main() -> int:
     ap.add_argument("--sweep-max-bytes", type=int, default=256 << 20)
     ap.add_argument("--sweep-ranks", type=int, default=16)
     ap.add_argument("--sweep-channels", type=int, default=16)
-    ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag"])
+    ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag", "wide"])
     ap.add_argument("--algo", default="auto", choices=["auto", "ring", "tree"],
                     help="all-reduce algorithm for --sweep (auto: the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -439,7 +439,7 @@ def main() -> int:
             "nchannels": w["nchannels"],
             "chunk_bytes": w["chunk_bytes"],
             "workgroups_per_channel": info["workgroups_per_channel"],
-            "proto": "bulk",
+            "proto": {1: "bulk", 2: "flag", 3: "wide"}.get(rs.comm_query(comm)["last_proto"], "?"),
             "parallelism": "1 GPU, simulated ranks",
         },
         "roofline": {

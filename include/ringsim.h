@@ -90,18 +90,23 @@ typedef enum {
   RINGSIM_MIN = 3
 } ringsim_redop_t;
 
-/* Protocols ("NCCL" book, s. 2.4): BULK keeps readiness in separate step
- * counters (Simple); FLAG packs a 4-byte flag with every 4 bytes of payload
- * so the receiver polls the data itself (LL). AUTO picks the protocol with
- * the lower predicted time (ringsim_debug_model), or FLAG below
- * flag_threshold_bytes per rank when a threshold is configured. FLAG uses a
- * chunk of min(chunk_bytes, 64 KiB); AUTO only picks it for all-reduces whose
- * per-channel share fits one tail loop either way, so AUTO's results do not
- * depend on the protocol it picks. */
+/* Protocols ("NCCL" book, s. 2.4; ch. 5 for their costs): BULK keeps
+ * readiness in separate step counters (Simple). FLAG packs a 4-byte flag with
+ * every 4 bytes of payload, so the receiver polls the data itself (LL: half
+ * of every line is payload). WIDE packs one 4-byte flag with 12 bytes of
+ * payload in each 16-byte line (8 bytes for int64), written and read as one
+ * 128-bit access: the MI355X counterpart of LL128, for medium messages.
+ * AUTO picks the protocol with the lowest predicted time
+ * (ringsim_debug_model), or FLAG below flag_threshold_bytes per rank and
+ * BULK above it when a threshold is configured. Every protocol walks the
+ * same chunks (FLAG and WIDE walk each loop in groups of 8 slot steps so that
+ * their FIFO never limits the chunk size), so results never depend on the
+ * protocol. */
 typedef enum {
   RINGSIM_PROTO_AUTO = 0,
   RINGSIM_PROTO_BULK = 1,
-  RINGSIM_PROTO_FLAG = 2
+  RINGSIM_PROTO_FLAG = 2,
+  RINGSIM_PROTO_WIDE = 3
 } ringsim_proto_t;
 
 /* All-reduce algorithms. RING is the ring schedule above. TREE is the double
@@ -153,11 +158,11 @@ typedef struct {
   size_t slot_bytes;
   size_t flag_threshold_bytes;
   size_t fifo_bytes;           /* bulk FIFO bytes in HBM */
-  size_t flag_fifo_bytes;      /* flag-packed FIFO bytes in HBM */
+  size_t flag_fifo_bytes;      /* flag-packed FIFO bytes in HBM (FLAG and WIDE share it) */
   int max_resident_workgroups; /* co-resident workgroups the device can hold */
   int compute_units;
   uint64_t calls;              /* collective calls enqueued so far */
-  int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG, 0 if none */
+  int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG/WIDE, 0 if none */
   int algo;                    /* configured all-reduce algorithm (ringsim_algo_t) */
   int tree_channels;           /* most channels per tree an all-reduce may use */
   size_t tree_fifo_bytes;      /* double-tree FIFO bytes in HBM */
@@ -234,13 +239,13 @@ const char* ringsim_get_error_string(ringsim_result_t result);
 
 /* Host-only cost model behind AUTO ("NCCL" book, ch. 5, ring.cc: latency =
  * hops x per-hop latency, bandwidth term = bytes moved / achievable bandwidth,
- * the flag protocol moving twice the FIFO bytes), with constants measured on
- * MI355X. Writes the predicted microseconds of one call of `coll`
- * (RINGSIM_COLL_ALLREDUCE, _REDUCE_SCATTER or _ALL_GATHER) with
- * `bytes_per_rank` bytes per rank (all-reduce buffer, reduce-scatter input,
- * all-gather output) on each protocol. Touches no device. */
+ * the FIFO bytes scaled by each line format: x2 for FLAG, x4/3 for WIDE),
+ * with constants measured on MI355X. Writes the predicted microseconds of one
+ * call of `coll` (RINGSIM_COLL_ALLREDUCE, _REDUCE_SCATTER or _ALL_GATHER)
+ * with `bytes_per_rank` bytes per rank (all-reduce buffer, reduce-scatter
+ * input, all-gather output) on each protocol. Touches no device. */
 ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t bytes_per_rank, double* us_bulk,
-                                     double* us_flag);
+                                     double* us_flag, double* us_wide);
 
 /* Host-only tree shape. Writes links[6] = (parent, first child, second
  * child) of `rank` in tree 0, then the same in tree 1 (-1 = none), for a

@@ -49,7 +49,7 @@ RESULT_NAMES = {
 DTYPES = {"int32": 0, "int64": 1, "float32": 2, "bfloat16": 3}
 ELEM_SIZE = {"int32": 4, "int64": 8, "float32": 4, "bfloat16": 2}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
-PROTOS = {"auto": 0, "bulk": 1, "flag": 2}
+PROTOS = {"auto": 0, "bulk": 1, "flag": 2, "wide": 3}
 ALGOS = {"auto": 0, "ring": 1, "tree": 2}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "alltoall": 3}
 
@@ -129,7 +129,8 @@ def lib() -> ctypes.CDLL:
         "ringsim_abort": (res, [vp]),
         "ringsim_get_error_string": (ctypes.c_char_p, [res]),
         "ringsim_debug_plan": (res, [i, sz, i, i, sz, i, ctypes.POINTER(ctypes.c_int64), sz, ctypes.POINTER(sz)]),
-        "ringsim_debug_model": (res, [i, i, i, sz, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+        "ringsim_debug_model": (res, [i, i, i, sz, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double)]),
         "ringsim_debug_tree": (res, [i, i, ctypes.POINTER(ctypes.c_int)]),
         "ringsim_debug_tree_model": (res, [i, i, sz, ctypes.POINTER(ctypes.c_double)]),
     }
@@ -297,10 +298,11 @@ def abort(comm: Comm) -> None:
 def debug_model(coll: str | int, nranks: int, nchannels: int, bytes_per_rank: int) -> dict:
     """Predicted microseconds per protocol (host-only cost model behind AUTO)."""
     c = COLLS[coll] if isinstance(coll, str) else int(coll)
-    b, f = ctypes.c_double(), ctypes.c_double()
-    _check(lib().ringsim_debug_model(c, nranks, nchannels, bytes_per_rank, ctypes.byref(b), ctypes.byref(f)),
+    b, f, w = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().ringsim_debug_model(c, nranks, nchannels, bytes_per_rank, ctypes.byref(b), ctypes.byref(f),
+                                     ctypes.byref(w)),
            "ringsim_debug_model")
-    return {"bulk_us": b.value, "flag_us": f.value}
+    return {"bulk_us": b.value, "flag_us": f.value, "wide_us": w.value}
 
 
 def debug_tree(nranks: int, rank: int) -> tuple[tuple[int, int, int], tuple[int, int, int]]:

@@ -1,0 +1,369 @@
+// ring_lines.hip -- ring kernels over flag-packed FIFO lines ("NCCL" book,
+// s. 2.4: LL and LL128 carry a flag inside the data, so the receiver polls
+// the data itself; ch. 5: LL moves half a line of payload, LL128 120 of 128
+// bytes). No tail counter and no fence sits on the data path: a line whose
+// flag equals the step's flag carries that step's payload. The consumer's
+// head counter is still published every few steps, for flow control only.
+//
+// Two line formats, both 16 bytes per lane:
+//   FLAG  two 8-byte words {4-byte payload, 4-byte flag}, each written and
+//         read as one 64-bit atomic access: 8 payload bytes per line.
+//   WIDE  {12 bytes of payload, 4-byte flag}, written and read as one
+//         128-bit device-coherent access: 12 payload bytes per line (8 for
+//         int64, whose elements never straddle two lines). This is the
+//         MI355X counterpart of LL128: NVLink delivers a warp's 128-byte
+//         line whole, and here the unit that arrives whole is one lane's
+//         naturally aligned 16-byte access, so the flag sits in every one.
+//
+// Lines carry a flag equal to the low 32 bits of (step + 1), taken from the
+// same monotonic step counters as the bulk protocol, so a line left over from
+// an earlier step (of either format) never matches: that would take 2^32
+// steps on one FIFO. Both formats share one FIFO array.
+//
+// Steps are walked group by group (StepIter groups): a stage moves at most
+// kLineGroupSteps slots before the next stage runs, which keeps one stage of
+// a workgroup inside the FIFO part that is always free, so the chunk (and
+// with it the partition and every result) is the same as the bulk
+// protocol's.
+#include "ringsim_device.h"
+
+namespace ringsim {
+
+namespace {
+
+// FIFO line accesses of the WIDE format: device-coherent (SC1) 128-bit
+// buffer accesses. Polling loops put a compiler fence before every re-read,
+// so that a load is never hoisted out of its loop.
+constexpr int kPolWideSt = 16;
+constexpr int kPolWideLd = 16;
+
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <int LP, int DT>
+struct LineFmt {
+  // payload dwords per 16-byte line
+  static constexpr int PD = LP == kLineFlag ? 2 : (DT == RINGSIM_INT64 ? 2 : 3);
+  static constexpr int PB = 4 * PD;
+};
+
+// One FIFO slot seen as 16-byte lines.
+template <int LP>
+struct Slot {
+  char* base;
+  rsrc_t rs;
+
+  __device__ __forceinline__ void init(const char* p, int bytes) {
+    base = const_cast<char*>(p);
+    if constexpr (LP == kLineWide) rs = make_rsrc(p, p ? bytes : 0);
+  }
+
+  // The raw 16 bytes of line li.
+  __device__ __forceinline__ u32x4 load(int li) const {
+    if constexpr (LP == kLineFlag) {
+      const uint64_t* w = reinterpret_cast<const uint64_t*>(base) + 2 * li;
+      const uint64_t v0 = ld_relaxed(w);
+      const uint64_t v1 = ld_relaxed(w + 1);
+      return u32x4{(uint32_t)v0, (uint32_t)(v0 >> 32), (uint32_t)v1, (uint32_t)(v1 >> 32)};
+    } else {
+      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, li * 16, 0, kPolWideLd));
+    }
+  }
+
+  static __device__ __forceinline__ bool ready(u32x4 v, uint32_t flag) {
+    if constexpr (LP == kLineFlag) return v.y == flag && v.w == flag;
+    else return v.w == flag;
+  }
+
+  static __device__ __forceinline__ u32x4 payload(u32x4 v) {
+    if constexpr (LP == kLineFlag) return u32x4{v.x, v.z, 0u, 0u};
+    else return u32x4{v.x, v.y, v.z, 0u};
+  }
+
+  __device__ __forceinline__ void store(int li, u32x4 x, uint32_t flag) const {
+    if constexpr (LP == kLineFlag) {
+      uint64_t* w = reinterpret_cast<uint64_t*>(base) + 2 * li;
+      st_relaxed(w, ((uint64_t)flag << 32) | x.x);
+      st_relaxed(w + 1, ((uint64_t)flag << 32) | x.y);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, flag}, rs, li * 16, 0, kPolWideSt);
+    }
+  }
+};
+
+// `valid` (<= PB) bytes of user data at p, as payload dwords; vector loads
+// when the whole line is valid and buffers are 16-byte aligned (then p is
+// 4-byte aligned), element loads otherwise.
+template <int DT, int PD>
+__device__ __forceinline__ u32x4 load_user(const char* p, int valid, int vec_ok) {
+  using T = typename Elem<DT>::T;
+  constexpr int PB = 4 * PD;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+  if (valid == PB && vec_ok) {
+    if constexpr (PD == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+      return u32x4{v.x, v.y, 0u, 0u};
+    } else {
+      return u32x4{w[0], w[1], w[2], 0u};
+    }
+  }
+  union {
+    u32x4 v;
+    T e[16 / sizeof(T)];
+  } u;
+  u.v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < PB / (int)sizeof(T); ++q)
+    if (q * (int)sizeof(T) < valid) u.e[q] = reinterpret_cast<const T*>(p)[q];
+  return u.v;
+}
+
+// Stores `valid` bytes of a line's payload to user data at p = base + off;
+// `ur` is a buffer resource over the step's output (whole 12-byte lines are
+// stored with one 96-bit access through it).
+template <int DT, int PD>
+__device__ __forceinline__ void store_user(char* p, rsrc_t ur, int off, u32x4 x, int valid, int vec_ok) {
+  using T = typename Elem<DT>::T;
+  constexpr int PB = 4 * PD;
+  if (valid == PB && vec_ok) {
+    if constexpr (PD == 2) *reinterpret_cast<u32x2*>(p) = u32x2{x.x, x.y};
+    else __builtin_amdgcn_raw_buffer_store_b96(u32x3{x.x, x.y, x.z}, ur, off, 0, 0);
+    return;
+  }
+  union {
+    u32x4 v;
+    T e[16 / sizeof(T)];
+  } u;
+  u.v = x;
+#pragma unroll
+  for (int q = 0; q < PB / (int)sizeof(T); ++q)
+    if (q * (int)sizeof(T) < valid) reinterpret_cast<T*>(p)[q] = u.e[q];
+}
+
+// op(a, b) on the payload dwords of one line.
+template <int DT, int OP, int PD>
+__device__ __forceinline__ u32x4 reduce_payload(u32x4 a, u32x4 b) {
+  if constexpr (PD == 2) {
+    const u32x2 z = VOp<DT, OP>::v2(u32x2{a.x, a.y}, u32x2{b.x, b.y});
+    return u32x4{z.x, z.y, 0u, 0u};
+  } else {
+    static_assert(DT != RINGSIM_INT64, "int64 lines carry two payload dwords");
+    return u32x4{VOp<DT, OP>::word(a.x, b.x), VOp<DT, OP>::word(a.y, b.y), VOp<DT, OP>::word(a.z, b.z), 0u};
+  }
+}
+
+}  // namespace
+
+template <int LP, int DT, int OP, int MODE>
+__global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
+  using T = typename Elem<DT>::T;
+  using F = LineFmt<LP, DT>;
+  constexpr int64_t E = sizeof(T);
+  constexpr int U = kFlagLinesPerThread;  // lines per thread in a full slot
+  const Pipe p = locate(a);
+  if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
+  __shared__ uint64_t s_base[2];
+  __shared__ uint64_t s_head;
+  if (threadIdx.x == 0) {
+    s_base[0] = ld_relaxed(&p.in_ctr->head);
+    s_base[1] = ld_relaxed(&p.out_ctr->tail);
+  }
+  __syncthreads();
+  const uint64_t in_base = s_base[0];
+  const uint64_t out_base = s_base[1];
+  const uint64_t nslots = (uint64_t)a.nslots;
+  uint64_t nrecv = 0, nsent = 0;
+  uint64_t head_known = out_base;  // uniform across the workgroup
+  uint64_t known_head = 0;         // thread 0
+  bool stop = false;               // per thread: stop waiting
+  const WaitCtx wc = wait_ctx(a);
+  uint32_t in_slot = (uint32_t)(in_base % nslots);
+  uint32_t out_slot = (uint32_t)(out_base % nslots);
+
+  const int64_t slice = (int64_t)(a.slot_bytes / 16) * F::PB / E;  // payload elements per slot
+  StepIter<DT, MODE> it;
+  it.init(a, p.r, p.c, p.w, slice, (int64_t)a.group * slice);
+  for (; !it.done; it.next()) {
+    const bool recv = it.recv, send = it.send;
+    if (send && nsent + 1 > nslots) {
+      const uint64_t need = out_base + nsent + 1 - nslots;
+      if (head_known < need) {  // uniform branch
+        if (threadIdx.x == 0) {
+          if (!stop && known_head < need) {
+            known_head = wait_geq(&p.out_ctr->head, need, wc);
+            stop = known_head == 0;
+          }
+          s_head = known_head > need ? known_head : need;
+        }
+        __syncthreads();
+        head_known = s_head;
+        __syncthreads();
+      }
+    }
+    const uint32_t flag_in = (uint32_t)(in_base + nrecv + 1);
+    const uint32_t flag_out = (uint32_t)(out_base + nsent + 1);
+    Slot<LP> fin, fout;
+    fin.init(recv ? p.in_fifo + (int64_t)in_slot * a.slot_bytes : nullptr, a.slot_bytes);
+    fout.init(send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr, a.slot_bytes);
+    const int64_t nbytes = it.ns() * E;
+    const int nlines = (int)div_up(nbytes, F::PB);  // <= kThreads * U
+    const char* lp = it.use_local ? it.local() : nullptr;
+    char* up = it.store ? it.out() : nullptr;
+    const rsrc_t ur = make_rsrc(up, up ? nbytes : 0);
+    if (nlines <= kThreads) {
+      // At most one line per thread (small messages): the shortest path from
+      // a flag's arrival to the next hop's store.
+      const int li = threadIdx.x;
+      if (li < nlines) {
+        const int valid = (int)min64(F::PB, nbytes - (int64_t)li * F::PB);
+        u32x4 loc = u32x4{0u, 0u, 0u, 0u};
+        if (lp) loc = load_user<DT, F::PD>(lp + (int64_t)li * F::PB, valid, a.vec_ok);
+        u32x4 x = loc;
+        if (recv) {
+          u32x4 v = fin.load(li);
+          if (!stop && !Slot<LP>::ready(v, flag_in)) {
+            const uint64_t t0 = wall_clock64();
+            uint32_t spins = 0;
+            while (!Slot<LP>::ready(v, flag_in)) {
+              if (give_up(wc, t0, ++spins)) {
+                stop = true;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+              compiler_fence();
+              v = fin.load(li);
+            }
+          }
+          x = Slot<LP>::payload(v);
+          if (lp) x = reduce_payload<DT, OP, F::PD>(x, loc);
+        }
+        if (send) fout.store(li, x, flag_out);
+        if (up) store_user<DT, F::PD>(up + (int64_t)li * F::PB, ur, li * F::PB, x, valid, a.vec_ok);
+      }
+    } else {
+      // Several lines per thread: thread t owns lines t, t + 256, ...; all
+      // of its own-operand loads and first polls are issued together, then
+      // only lines whose flags have not arrived are polled again.
+      u32x4 x[U];
+      u32x4 loc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int li = threadIdx.x + u * kThreads;
+        loc[u] = u32x4{0u, 0u, 0u, 0u};
+        if (lp && li < nlines)
+          loc[u] = load_user<DT, F::PD>(lp + (int64_t)li * F::PB, (int)min64(F::PB, nbytes - (int64_t)li * F::PB),
+                                        a.vec_ok);
+      }
+      if (recv) {
+        u32x4 v[U];
+        uint32_t pending = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int li = threadIdx.x + u * kThreads;
+          v[u] = u32x4{0u, 0u, 0u, 0u};
+          if (li < nlines) {
+            v[u] = fin.load(li);
+            if (!Slot<LP>::ready(v[u], flag_in)) pending |= 1u << u;
+          }
+        }
+        if (pending && !stop) {
+          const uint64_t t0 = wall_clock64();
+          uint32_t spins = 0;
+          while (pending) {
+            if (give_up(wc, t0, ++spins)) {
+              stop = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            compiler_fence();
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              if (pending & (1u << u)) {
+                v[u] = fin.load(threadIdx.x + u * kThreads);
+                if (Slot<LP>::ready(v[u], flag_in)) pending &= ~(1u << u);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          x[u] = Slot<LP>::payload(v[u]);
+          if (lp) x[u] = reduce_payload<DT, OP, F::PD>(x[u], loc[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = loc[u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int li = threadIdx.x + u * kThreads;
+        if (li < nlines) {
+          if (send) fout.store(li, x[u], flag_out);
+          if (up)
+            store_user<DT, F::PD>(up + (int64_t)li * F::PB, ur, li * F::PB, x[u],
+                                  (int)min64(F::PB, nbytes - (int64_t)li * F::PB), a.vec_ok);
+        }
+      }
+    }
+    if (recv) {
+      ++nrecv;
+      in_slot = in_slot + 1 == (uint32_t)nslots ? 0 : in_slot + 1;
+      if (nrecv % kFlagHeadEvery == 0) {  // uniform: release drained slots
+        __syncthreads();
+        if (threadIdx.x == 0) st_relaxed(&p.in_ctr->head, in_base + nrecv);
+      }
+    }
+    if (send) {
+      ++nsent;
+      out_slot = out_slot + 1 == (uint32_t)nslots ? 0 : out_slot + 1;
+    }
+  }
+  // Leave both counters at the number of steps this call moved, so the next
+  // call (any protocol) starts from the same base on both sides.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st_relaxed(&p.in_ctr->head, in_base + nrecv);
+    st_relaxed(&p.out_ctr->tail, out_base + nsent);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+
+template <int LP>
+struct LineLaunch {
+  template <int DT, int OP, int MODE>
+  static hipError_t run(const RingArgs& a, hipStream_t s) {
+    const int grid = a.nranks * a.nchannels * a.wpc;
+    hipLaunchKernelGGL((ring_line_kernel<LP, DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+};
+
+hipError_t launch_ring_lines(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s) {
+  if (line_proto == kLineWide) return dispatch_ring<LineLaunch<kLineWide>>(a, mode, dtype, op, s);
+  return dispatch_ring<LineLaunch<kLineFlag>>(a, mode, dtype, op, s);
+}
+
+int line_blocks_per_cu() {
+  int m = 1 << 30;
+  auto acc = [&](int v) { m = v < m ? v : m; };
+#define RS_OCC_LINE(LP, DT)                                                  \
+  acc(occupancy(ring_line_kernel<LP, DT, RINGSIM_SUM, kAllReduce>, 0));      \
+  acc(occupancy(ring_line_kernel<LP, DT, RINGSIM_MIN, kReduceScatter>, 0));  \
+  acc(occupancy(ring_line_kernel<LP, DT, RINGSIM_SUM, kAllGather>, 0));
+  RS_OCC_LINE(kLineFlag, RINGSIM_INT32)
+  RS_OCC_LINE(kLineFlag, RINGSIM_INT64)
+  RS_OCC_LINE(kLineFlag, RINGSIM_FLOAT32)
+  RS_OCC_LINE(kLineFlag, RINGSIM_BFLOAT16)
+  RS_OCC_LINE(kLineWide, RINGSIM_INT32)
+  RS_OCC_LINE(kLineWide, RINGSIM_INT64)
+  RS_OCC_LINE(kLineWide, RINGSIM_FLOAT32)
+  RS_OCC_LINE(kLineWide, RINGSIM_BFLOAT16)
+#undef RS_OCC_LINE
+  return m == (1 << 30) ? 0 : m;
+}
+
+}  // namespace ringsim

@@ -3,17 +3,19 @@
 // Form of the model: "NCCL" book (aireadcode.com), ch. 5, ring.cc -- a ring
 // collective's latency is nSteps hops of a per-hop latency, its bandwidth term
 // is the bytes it moves over the achievable bandwidth (bus bandwidth times
-// nRanks / nSteps), and the flag-packed (LL) protocol pays half the bandwidth
-// because every 4 bytes of payload travel with a 4-byte flag. Here:
+// nRanks / nSteps), and the flag-packed protocols pay for their flags: LL
+// half the bandwidth, LL128 a sixteenth. Here:
 //
 //   t(proto) = base + hops * hop_latency(proto) + bytes(proto) / bandwidth(proto)
 //
 // with hops = 2(N-1) for the all-reduce and N-1 for reduce-scatter and
-// all-gather, bytes = the HBM bytes of the method (flag protocol: FIFO bytes
-// doubled), and constants fitted to bench.py --sweep on MI355X (16 / 8 / 4
-// ranks, 4..16 channels): a flag hop costs ~1.7 us and a bulk hop ~2.7 us
-// when every chunk of the ring is busy; one flag-path workgroup sustains
-// ~13 GB/s of method bytes, the bulk kernel ~6.9 TB/s in total.
+// all-gather, bytes = the HBM bytes of the method (FIFO bytes scaled by the
+// line format: x2 for the flag protocol's 8-of-16-byte lines, x4/3 for the
+// wide protocol's 12-of-16), and constants fitted to bench.py --sweep on
+// MI355X (16 / 8 / 4 ranks, 4..16 channels): when every chunk of the ring is
+// busy a flag hop costs ~1.5 us, a wide hop ~1.85 us and a bulk hop ~2.7 us;
+// one line-protocol workgroup sustains ~10.5 (flag) or ~11.5 (wide) GB/s of
+// method bytes, the bulk kernel ~6.9 TB/s in total.
 #pragma once
 
 #include <algorithm>
@@ -21,33 +23,37 @@
 
 namespace ringsim {
 
+enum ModelProto : int { kModelBulk = 0, kModelFlag = 1, kModelWide = 2 };
+
 struct RingModel {
   double base_us = 3.0;
-  double hop_us_flag = 1.7;
-  double hop_us_bulk = 2.7;
-  double flag_wg_gbs = 13.0;     // per (rank, channel) workgroup
-  double flag_max_gbs = 4000.0;  // flag path ceiling
+  double hop_us[3] = {2.7, 1.5, 1.85};   // bulk, flag, wide
+  double wg_gbs[3] = {0.0, 10.5, 11.5};  // line protocols: per (rank, channel) workgroup
+  double line_max_gbs = 4000.0;          // line protocols' ceiling
   double bulk_gbs = 6900.0;
 };
 
 enum ModelColl : int { kModelAllReduce = 0, kModelReduceScatter = 1, kModelAllGather = 2 };
 
+// FIFO bytes per payload byte of each protocol's slots.
+inline double fifo_factor(int proto) { return proto == kModelFlag ? 2.0 : proto == kModelWide ? 4.0 / 3.0 : 1.0; }
+
 // Method bytes of one call with S bytes per rank (all-reduce buffer,
 // reduce-scatter input, all-gather output), summed over ranks.
-inline double model_bytes(int coll, int nranks, double s, bool flag) {
+inline double model_bytes(int coll, int nranks, double s, int proto) {
   const double n = nranks;
   const double fifo = (coll == kModelAllReduce ? 4.0 * (n - 1.0) : 2.0 * (n - 1.0)) * s;
   const double user = coll == kModelAllReduce ? 2.0 * n * s : (n + 1.0) * s;
-  return user + (flag ? 2.0 : 1.0) * fifo;
+  return user + fifo_factor(proto) * fifo;
 }
 
 // Predicted microseconds of one call.
-inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, double bytes_per_rank, bool flag) {
+inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, double bytes_per_rank, int proto) {
   if (nranks <= 1) return m.base_us;
   const double hops = coll == kModelAllReduce ? 2.0 * (nranks - 1) : (double)(nranks - 1);
-  const double bytes = model_bytes(coll, nranks, bytes_per_rank, flag);
-  const double gbs = flag ? std::min(m.flag_max_gbs, m.flag_wg_gbs * nranks * nchannels) : m.bulk_gbs;
-  return m.base_us + hops * (flag ? m.hop_us_flag : m.hop_us_bulk) + bytes / (gbs * 1e3);
+  const double bytes = model_bytes(coll, nranks, bytes_per_rank, proto);
+  const double gbs = proto == kModelBulk ? m.bulk_gbs : std::min(m.line_max_gbs, m.wg_gbs[proto] * nranks * nchannels);
+  return m.base_us + hops * m.hop_us[proto] + bytes / (gbs * 1e3);
 }
 
 // Predicted microseconds of a double-binary-tree all-reduce: the reduce
@@ -56,9 +62,9 @@ inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, 
 // tree_channels workgroups (two trees, an up and a down role each).
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double bytes_per_rank) {
   if (nranks <= 1) return m.base_us;
-  const double bytes = model_bytes(kModelAllReduce, nranks, bytes_per_rank, true);
-  const double gbs = std::min(m.flag_max_gbs, m.flag_wg_gbs * 4.0 * nranks * tree_channels);
-  return m.base_us + 2.0 * depth * m.hop_us_flag + bytes / (gbs * 1e3);
+  const double bytes = model_bytes(kModelAllReduce, nranks, bytes_per_rank, kModelFlag);
+  const double gbs = std::min(m.line_max_gbs, m.wg_gbs[kModelFlag] * 4.0 * nranks * tree_channels);
+  return m.base_us + 2.0 * depth * m.hop_us[kModelFlag] + bytes / (gbs * 1e3);
 }
 
 }  // namespace ringsim

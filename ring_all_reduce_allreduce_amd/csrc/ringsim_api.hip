@@ -190,32 +190,43 @@ void fill_common(const ringsim_comm* c, RingArgs* a, const void* const* sb, void
   a->skip_rank = c->skip_rank;
 }
 
-// AUTO's choice: a fixed threshold when one was configured, else the cost
-// model. The flag protocol caps its chunk at kFlagChunkBytes; it is only
-// chosen while every channel's share fits in one tail loop under both chunk
-// sizes, so the partition -- and every floating-point result -- is the same
-// whichever protocol runs.
-bool auto_picks_flag(const ringsim_comm* c, int mode, size_t bytes_per_rank) {
-  if (c->flag_threshold) return bytes_per_rank < c->flag_threshold;
-  const size_t limit = (size_t)c->nranks * c->nchannels * std::min<size_t>(c->chunk_bytes, kFlagChunkBytes);
-  if (mode == kAllReduce && bytes_per_rank >= limit) return false;
+// The protocol of one call. A fixed protocol is taken as configured; AUTO
+// takes the flag protocol below a configured threshold and bulk above it,
+// else the protocol the cost model predicts fastest. Every protocol walks the
+// same partition (the line protocols walk each loop in groups of
+// kLineGroupSteps slots), so the choice never changes a result bit.
+int pick_proto(const ringsim_comm* c, int mode, size_t bytes_per_rank) {
+  if (c->proto != RINGSIM_PROTO_AUTO) return c->proto;
+  if (c->flag_threshold) return bytes_per_rank < c->flag_threshold ? RINGSIM_PROTO_FLAG : RINGSIM_PROTO_BULK;
   const RingModel m;
-  return model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, true) <
-         model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, false);
+  int best = RINGSIM_PROTO_BULK;
+  double best_us = model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, kModelBulk);
+  const int line_protos[2][2] = {{RINGSIM_PROTO_FLAG, kModelFlag}, {RINGSIM_PROTO_WIDE, kModelWide}};
+  for (const auto& lp : line_protos) {
+    const double us = model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, lp[1]);
+    if (us < best_us) {
+      best_us = us;
+      best = lp[0];
+    }
+  }
+  return best;
 }
 
-// Picks the protocol and fills the protocol-dependent launch geometry.
-void fill_proto(const ringsim_comm* c, RingArgs* a, int mode, size_t bytes_per_rank, int esize, bool* flag) {
-  const bool f = c->proto == RINGSIM_PROTO_FLAG || (c->proto == RINGSIM_PROTO_AUTO && auto_picks_flag(c, mode, bytes_per_rank));
-  *flag = f;
-  if (f) {
+int model_proto(int proto) {
+  return proto == RINGSIM_PROTO_FLAG ? kModelFlag : proto == RINGSIM_PROTO_WIDE ? kModelWide : kModelBulk;
+}
+
+// Fills the protocol-dependent launch geometry.
+void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize) {
+  a->chunk = (int64_t)c->chunk_bytes / esize;
+  if (proto == RINGSIM_PROTO_FLAG || proto == RINGSIM_PROTO_WIDE) {
     a->wpc = 1;
     a->fifo = c->flag_fifo;
     a->fifo_stride = c->nchannels;
     a->fifo_mul = 1;
     a->nslots = kFlagSlots;
     a->slot_bytes = kFlagSlotBytes;
-    a->chunk = (int64_t)std::min<size_t>(c->chunk_bytes, (size_t)kFlagChunkBytes) / esize;
+    a->group = kLineGroupSteps;
   } else {
     a->wpc = c->wpc;
     a->fifo = c->fifo;
@@ -223,8 +234,8 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int mode, size_t bytes_per_r
     a->fifo_mul = c->wpc;
     a->nslots = c->nslots;
     a->slot_bytes = (int)c->slot_bytes;
-    a->chunk = (int64_t)c->chunk_bytes / esize;
     a->lds_stage = c->lds_stage;
+    a->group = 0;
   }
 }
 
@@ -255,18 +266,18 @@ int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank) {
 // Predicted time of the ring as AUTO would run it.
 double ring_auto_us(const ringsim_comm* c, size_t bytes_per_rank) {
   const RingModel m;
-  const bool flag = c->proto == RINGSIM_PROTO_FLAG ||
-                    (c->proto == RINGSIM_PROTO_AUTO && auto_picks_flag(c, kAllReduce, bytes_per_rank));
-  return model_us(m, kAllReduce, c->nranks, c->nchannels, (double)bytes_per_rank, flag);
+  const int proto = pick_proto(c, kAllReduce, bytes_per_rank);
+  return model_us(m, kAllReduce, c->nranks, c->nchannels, (double)bytes_per_rank, model_proto(proto));
 }
 
 // AUTO's algorithm: the tree only where the fold order cannot show in the
 // result (integers wrap associatively; max/min pick one input), only when
-// the flag-packed lines it moves are allowed, and only when it is predicted
-// to be faster than the ring.
+// the flag-packed lines it moves are allowed (protocol AUTO or FLAG), and
+// only when it is predicted to be faster than the ring.
 bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t bytes_per_rank) {
   const bool order_free = dtype == RINGSIM_INT32 || dtype == RINGSIM_INT64 || op == RINGSIM_MAX || op == RINGSIM_MIN;
-  if (!order_free || c->proto == RINGSIM_PROTO_BULK || c->tree_channels < 1) return false;
+  const bool lines_ok = c->proto == RINGSIM_PROTO_AUTO || c->proto == RINGSIM_PROTO_FLAG;
+  if (!order_free || !lines_ok || c->tree_channels < 1) return false;
   const RingModel m;
   return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank), (double)bytes_per_rank) <
          ring_auto_us(c, bytes_per_rank);
@@ -335,13 +346,16 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   RingArgs a;
   fill_common(c, &a, sb, rb);
   a.count = (int64_t)count;
-  bool flag = false;
-  fill_proto(c, &a, mode, per_rank_bytes, esize, &flag);
+  const int proto = pick_proto(c, mode, per_rank_bytes);
+  fill_proto(c, &a, proto, esize);
   // Vector moves need every unit to start on a 16-byte boundary; for the
   // block-strided collectives that requires whole 16-byte blocks.
   a.vec_ok = vec && (mode == kAllReduce || (count * esize) % 16 == 0);
-  c->last_proto = flag ? RINGSIM_PROTO_FLAG : RINGSIM_PROTO_BULK;
-  const hipError_t e = flag ? launch_ring_flag(a, mode, dtype, op, s) : launch_ring_bulk(a, mode, dtype, op, s);
+  c->last_proto = proto;
+  const hipError_t e =
+      proto == RINGSIM_PROTO_BULK
+          ? launch_ring_bulk(a, mode, dtype, op, s)
+          : launch_ring_lines(a, proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag, mode, dtype, op, s);
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "kernel launch failed: %s", hipGetErrorString(e));
     return RINGSIM_UNHANDLED_DEVICE_ERROR;
@@ -391,7 +405,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   if (!comm) return RINGSIM_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > RINGSIM_MAX_RANKS) return RINGSIM_INVALID_ARGUMENT;
   if (nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS) return RINGSIM_INVALID_ARGUMENT;
-  if (proto < RINGSIM_PROTO_AUTO || proto > RINGSIM_PROTO_FLAG) return RINGSIM_INVALID_ARGUMENT;
+  if (proto < RINGSIM_PROTO_AUTO || proto > RINGSIM_PROTO_WIDE) return RINGSIM_INVALID_ARGUMENT;
   ringsim_config_t cfg;
   ringsim_config_default(&cfg);
   if (user_cfg) {
@@ -423,7 +437,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Bulk steps stage their own operand in LDS (double-buffered) unless the
   // slot is too large or RINGSIM_LDS_STAGE=0.
   const int lds_stage = cfg.slot_bytes <= (size_t)kMaxStagedSlotBytes && env_long("RINGSIM_LDS_STAGE", 1) != 0;
-  const int per_cu = ring_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0);
+  const int per_cu = std::min(bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_blocks_per_cu());
   if (per_cu <= 0) return RINGSIM_UNHANDLED_DEVICE_ERROR;
   const int64_t max_resident = (int64_t)per_cu * cus;
 
@@ -665,14 +679,15 @@ const char* ringsim_get_error_string(ringsim_result_t result) {
 }
 
 ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t bytes_per_rank, double* us_bulk,
-                                     double* us_flag) {
-  if (!us_bulk || !us_flag) return RINGSIM_INVALID_ARGUMENT;
+                                     double* us_flag, double* us_wide) {
+  if (!us_bulk || !us_flag || !us_wide) return RINGSIM_INVALID_ARGUMENT;
   if (coll < RINGSIM_COLL_ALLREDUCE || coll > RINGSIM_COLL_ALL_GATHER) return RINGSIM_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS)
     return RINGSIM_INVALID_ARGUMENT;
   const RingModel m;
-  *us_bulk = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, false);
-  *us_flag = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, true);
+  *us_bulk = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, kModelBulk);
+  *us_flag = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, kModelFlag);
+  *us_wide = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, kModelWide);
   return RINGSIM_SUCCESS;
 }
 

@@ -15,10 +15,14 @@ constexpr int kDefaultSlots = 8;      // FIFO depth (NCCL_STEPS)
 constexpr int kFlagLinesPerThread = 4;  // flag-packed: 16-byte lines per thread per slot
 constexpr int kFlagSlotBytes = kThreads * kFlagLinesPerThread * 16;  // 16 KiB (8 KiB payload)
 constexpr int kFlagSlots = 16;
-constexpr int kFlagHeadEvery = kFlagSlots / 2;  // flag path publishes head every this many steps
-// Largest chunk the flag path may use: one stage of a workgroup must fit in
-// the FIFO part that is always free while both neighbours sit in stage 0.
-constexpr int kFlagChunkBytes = (kFlagSlots - kFlagHeadEvery) * (kFlagSlotBytes / 2);  // 64 KiB
+constexpr int kFlagHeadEvery = kFlagSlots / 2;  // line protocols publish head every this many steps
+// Slots one stage of a line-protocol workgroup moves before the next stage
+// runs: it must fit in the FIFO part that is always free while both
+// neighbours sit in stage 0 (the rest may hold drained but unpublished steps).
+constexpr int kLineGroupSteps = kFlagSlots - kFlagHeadEvery;
+
+// Line formats of the flag-packed protocols (16 bytes per line).
+enum LineProto : int { kLineFlag = 0, kLineWide = 1 };
 
 // Step counters of one FIFO (sender -> receiver, pipeline). The producer owns
 // `tail` (slots filled), the consumer owns `head` (slots drained). Each sits
@@ -60,6 +64,7 @@ struct RingArgs {
   uint64_t timeout_ticks;  // bound on one wait, in wall-clock ticks
   int skip_rank;        // testing knob: workgroups of this rank return at once (-1 = none)
   int lds_stage;        // bulk: stage each step's own operand in LDS (2 x slot_bytes dynamic LDS)
+  int group;            // slot steps a stage moves before the next stage runs (0 = the whole stage)
 };
 
 // Double-binary-tree all-reduce (flag-packed lines). Workgroup b of the grid
@@ -100,16 +105,16 @@ struct CopyArgs {
   int vec_ok;
 };
 
-// Kernel launchers (ringsim_kernels.hip).
+// Kernel launchers (ring_bulk.hip, ring_lines.hip, tree_flag.hip, copy.hip).
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
-hipError_t launch_ring_flag(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
+hipError_t launch_ring_lines(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_tree_flag(const TreeArgs& a, int dtype, int op, hipStream_t s);
-// Max co-resident tree workgroups per CU over every dtype and op.
+// Max co-resident workgroups per CU over every instantiation of a kernel
+// family (the bulk kernels launched with `lds_bytes` of dynamic LDS).
 int tree_blocks_per_cu();
-// Max co-resident workgroups per CU over every ring kernel instantiation, the
-// bulk kernels launched with `bulk_lds_bytes` of dynamic LDS.
-int ring_blocks_per_cu(size_t bulk_lds_bytes);
+int bulk_blocks_per_cu(size_t lds_bytes);
+int line_blocks_per_cu();
 // Largest bulk slot that is staged in LDS (two buffers must fit beside a
 // second workgroup's on the 160 KiB of a CU).
 constexpr int kMaxStagedSlotBytes = 64 * 1024;

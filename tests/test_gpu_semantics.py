@@ -75,7 +75,7 @@ def test_call_returns_before_completion_and_keeps_stream_order():
         rs.comm_destroy(comm)
 
 
-@pytest.mark.parametrize("proto", ["bulk", "flag"])
+@pytest.mark.parametrize("proto", ["bulk", "flag", "wide"])
 def test_missing_rank_times_out_and_poisons_the_comm(proto, monkeypatch):
     import torch
 
