@@ -248,6 +248,8 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
 // Host-side dispatch
 // ---------------------------------------------------------------------------
 
+namespace {
+
 struct BulkLaunch {
   template <int DT, int OP, int MODE>
   static hipError_t run(const RingArgs& a, hipStream_t s) {
@@ -257,6 +259,8 @@ struct BulkLaunch {
     return hipGetLastError();
   }
 };
+
+}  // namespace
 
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s) {
   return dispatch_ring<BulkLaunch>(a, mode, dtype, op, s);

@@ -1,4 +1,4 @@
-// ring_lines.hip -- ring kernels over flag-packed FIFO lines ("NCCL" book,
+// ring_lines.h -- ring kernels over flag-packed FIFO lines ("NCCL" book,
 // s. 2.4: LL and LL128 carry a flag inside the data, so the receiver polls
 // the data itself; ch. 5: LL moves half a line of payload, LL128 120 of 128
 // bytes). No tail counter and no fence sits on the data path: a line whose
@@ -25,6 +25,8 @@
 // a workgroup inside the FIFO part that is always free, so the chunk (and
 // with it the partition and every result) is the same as the bulk
 // protocol's.
+#pragma once
+
 #include "ringsim_device.h"
 
 namespace ringsim {
@@ -155,7 +157,10 @@ __device__ __forceinline__ u32x4 reduce_payload(u32x4 a, u32x4 b) {
 
 }  // namespace
 
-template <int LP, int DT, int OP, int MODE>
+// ONE: the host has checked that no step of this launch holds more than one
+// line per thread, so only the one-line path is compiled; otherwise every
+// step takes the several-lines path.
+template <int LP, bool ONE, int DT, int OP, int MODE>
 __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
   using F = LineFmt<LP, DT>;
@@ -211,7 +216,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
     const char* lp = it.use_local ? it.local() : nullptr;
     char* up = it.store ? it.out() : nullptr;
     const rsrc_t ur = make_rsrc(up, up ? nbytes : 0);
-    if (nlines <= kThreads) {
+    if constexpr (ONE) {
       // At most one line per thread (small messages): the shortest path from
       // a flag's arrival to the next hop's store.
       const int li = threadIdx.x;
@@ -244,7 +249,9 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
     } else {
       // Several lines per thread: thread t owns lines t, t + 256, ...; all
       // of its own-operand loads and first polls are issued together, then
-      // only lines whose flags have not arrived are polled again.
+      // only lines whose flags have not arrived are polled again, every
+      // round issuing all of its loads before it checks any of them (one
+      // load latency per round, not per line).
       u32x4 x[U];
       u32x4 loc[U];
 #pragma unroll
@@ -260,30 +267,34 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
         uint32_t pending = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int li = threadIdx.x + u * kThreads;
           v[u] = u32x4{0u, 0u, 0u, 0u};
-          if (li < nlines) {
-            v[u] = fin.load(li);
-            if (!Slot<LP>::ready(v[u], flag_in)) pending |= 1u << u;
-          }
+          if (threadIdx.x + u * kThreads < nlines) v[u] = fin.load(threadIdx.x + u * kThreads);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (threadIdx.x + u * kThreads < nlines && !Slot<LP>::ready(v[u], flag_in)) pending |= 1u << u;
         if (pending && !stop) {
           const uint64_t t0 = wall_clock64();
-          uint32_t spins = 0;
+          uint32_t spins = 0, verdict = 0;
           while (pending) {
-            if (give_up(wc, t0, ++spins)) {
-              stop = true;
-              break;
-            }
+            if ((verdict = wait_verdict(wc, t0, ++spins)) != 0u) break;
             __builtin_amdgcn_s_sleep(1);
             compiler_fence();
+            u32x4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (pending & (1u << u)) w[u] = fin.load(threadIdx.x + u * kThreads);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-              if (pending & (1u << u)) {
-                v[u] = fin.load(threadIdx.x + u * kThreads);
-                if (Slot<LP>::ready(v[u], flag_in)) pending &= ~(1u << u);
+              if ((pending & (1u << u)) && Slot<LP>::ready(w[u], flag_in)) {
+                v[u] = w[u];
+                pending &= ~(1u << u);
               }
             }
+          }
+          if (verdict) {
+            stop = true;
+            if (verdict != kStopQuiet) raise_error(wc, verdict);
           }
         }
 #pragma unroll
@@ -326,44 +337,6 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
     st_relaxed(&p.in_ctr->head, in_base + nrecv);
     st_relaxed(&p.out_ctr->tail, out_base + nsent);
   }
-}
-
-// ---------------------------------------------------------------------------
-// Host-side dispatch
-// ---------------------------------------------------------------------------
-
-template <int LP>
-struct LineLaunch {
-  template <int DT, int OP, int MODE>
-  static hipError_t run(const RingArgs& a, hipStream_t s) {
-    const int grid = a.nranks * a.nchannels * a.wpc;
-    hipLaunchKernelGGL((ring_line_kernel<LP, DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-};
-
-hipError_t launch_ring_lines(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s) {
-  if (line_proto == kLineWide) return dispatch_ring<LineLaunch<kLineWide>>(a, mode, dtype, op, s);
-  return dispatch_ring<LineLaunch<kLineFlag>>(a, mode, dtype, op, s);
-}
-
-int line_blocks_per_cu() {
-  int m = 1 << 30;
-  auto acc = [&](int v) { m = v < m ? v : m; };
-#define RS_OCC_LINE(LP, DT)                                                  \
-  acc(occupancy(ring_line_kernel<LP, DT, RINGSIM_SUM, kAllReduce>, 0));      \
-  acc(occupancy(ring_line_kernel<LP, DT, RINGSIM_MIN, kReduceScatter>, 0));  \
-  acc(occupancy(ring_line_kernel<LP, DT, RINGSIM_SUM, kAllGather>, 0));
-  RS_OCC_LINE(kLineFlag, RINGSIM_INT32)
-  RS_OCC_LINE(kLineFlag, RINGSIM_INT64)
-  RS_OCC_LINE(kLineFlag, RINGSIM_FLOAT32)
-  RS_OCC_LINE(kLineFlag, RINGSIM_BFLOAT16)
-  RS_OCC_LINE(kLineWide, RINGSIM_INT32)
-  RS_OCC_LINE(kLineWide, RINGSIM_INT64)
-  RS_OCC_LINE(kLineWide, RINGSIM_FLOAT32)
-  RS_OCC_LINE(kLineWide, RINGSIM_BFLOAT16)
-#undef RS_OCC_LINE
-  return m == (1 << 30) ? 0 : m;
 }
 
 }  // namespace ringsim

@@ -4,21 +4,24 @@
 // collective's latency is nSteps hops of a per-hop latency, its bandwidth term
 // is the bytes it moves over the achievable bandwidth (bus bandwidth times
 // nRanks / nSteps), and the flag-packed protocols pay for their flags: LL
-// half the bandwidth, LL128 a sixteenth. Here:
+// half the bandwidth, LL128 a sixteenth. Here the two terms overlap (the
+// ring pipelines steps while the first chunks are still in flight), so they
+// are combined as a 2-norm rather than added:
 //
-//   t(proto) = base + hops * hop_latency(proto) + bytes(proto) / bandwidth(proto)
+//   t(proto) = base + sqrt((hops * hop_latency)^2 + (bytes / bandwidth)^2)
 //
 // with hops = 2(N-1) for the all-reduce and N-1 for reduce-scatter and
 // all-gather, bytes = the HBM bytes of the method (FIFO bytes scaled by the
 // line format: x2 for the flag protocol's 8-of-16-byte lines, x4/3 for the
 // wide protocol's 12-of-16), and constants fitted to bench.py --sweep on
-// MI355X (16 / 8 / 4 ranks, 4..16 channels): when every chunk of the ring is
-// busy a flag hop costs ~1.5 us, a wide hop ~1.85 us and a bulk hop ~2.7 us;
-// one line-protocol workgroup sustains ~10.5 (flag) or ~11.5 (wide) GB/s of
-// method bytes, the bulk kernel ~6.9 TB/s in total.
+// MI355X (16 and 8 ranks and channels, 8 B .. 64 MiB per rank): a hop costs
+// ~1.37 us (flag), ~1.65 us (wide) or ~2.45 us (bulk) when every chunk of
+// the ring is busy; one line-protocol workgroup sustains ~11.5 (flag) or
+// ~14 (wide) GB/s of method bytes, the bulk kernel ~6.9 TB/s in total.
 #pragma once
 
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 
 namespace ringsim {
@@ -27,10 +30,13 @@ enum ModelProto : int { kModelBulk = 0, kModelFlag = 1, kModelWide = 2 };
 
 struct RingModel {
   double base_us = 3.0;
-  double hop_us[3] = {2.7, 1.5, 1.85};   // bulk, flag, wide
-  double wg_gbs[3] = {0.0, 10.5, 11.5};  // line protocols: per (rank, channel) workgroup
-  double line_max_gbs = 4000.0;          // line protocols' ceiling
+  double hop_us[3] = {2.45, 1.37, 1.65};  // bulk, flag, wide
+  double wg_gbs[3] = {0.0, 11.5, 14.0};   // line protocols: per (rank, channel) workgroup
+  double line_max_gbs = 4000.0;           // line protocols' ceiling
   double bulk_gbs = 6900.0;
+  // Double-binary tree (flag lines): per-hop latency and per-workgroup rate.
+  double tree_hop_us = 1.7;
+  double tree_wg_gbs = 13.0;
 };
 
 enum ModelColl : int { kModelAllReduce = 0, kModelReduceScatter = 1, kModelAllGather = 2 };
@@ -53,7 +59,7 @@ inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, 
   const double hops = coll == kModelAllReduce ? 2.0 * (nranks - 1) : (double)(nranks - 1);
   const double bytes = model_bytes(coll, nranks, bytes_per_rank, proto);
   const double gbs = proto == kModelBulk ? m.bulk_gbs : std::min(m.line_max_gbs, m.wg_gbs[proto] * nranks * nchannels);
-  return m.base_us + hops * m.hop_us[proto] + bytes / (gbs * 1e3);
+  return m.base_us + std::hypot(hops * m.hop_us[proto], bytes / (gbs * 1e3));
 }
 
 // Predicted microseconds of a double-binary-tree all-reduce: the reduce
@@ -63,8 +69,8 @@ inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, 
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double bytes_per_rank) {
   if (nranks <= 1) return m.base_us;
   const double bytes = model_bytes(kModelAllReduce, nranks, bytes_per_rank, kModelFlag);
-  const double gbs = std::min(m.line_max_gbs, m.wg_gbs[kModelFlag] * 4.0 * nranks * tree_channels);
-  return m.base_us + 2.0 * depth * m.hop_us[kModelFlag] + bytes / (gbs * 1e3);
+  const double gbs = std::min(m.line_max_gbs, m.tree_wg_gbs * 4.0 * nranks * tree_channels);
+  return m.base_us + 2.0 * depth * m.tree_hop_us + bytes / (gbs * 1e3);
 }
 
 }  // namespace ringsim

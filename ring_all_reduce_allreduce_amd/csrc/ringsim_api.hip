@@ -239,6 +239,16 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize) {
   }
 }
 
+// Longest unit (bytes) any workgroup of a ring launch moves in one stage; no
+// step is longer. The first loop of channel 0 (the longest channel) holds
+// the longest units.
+int64_t max_unit_bytes(const RingArgs& a, int mode, int esize) {
+  const int64_t A = 16 / esize;
+  const int64_t l0 = channel_span(a.count, a.nchannels, A);
+  const int64_t cur = mode == kAllReduce ? ar_loop_chunk(l0, a.nranks, a.chunk, A) : min64(a.chunk, l0);
+  return align_up(div_up(cur, a.wpc), A) * esize;
+}
+
 ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void* const* rb, size_t bytes,
                                    hipStream_t s) {
   if (sb[0] == rb[0] || bytes == 0) return RINGSIM_SUCCESS;
@@ -352,10 +362,16 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   // block-strided collectives that requires whole 16-byte blocks.
   a.vec_ok = vec && (mode == kAllReduce || (count * esize) % 16 == 0);
   c->last_proto = proto;
-  const hipError_t e =
-      proto == RINGSIM_PROTO_BULK
-          ? launch_ring_bulk(a, mode, dtype, op, s)
-          : launch_ring_lines(a, proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag, mode, dtype, op, s);
+  hipError_t e;
+  if (proto == RINGSIM_PROTO_BULK) {
+    e = launch_ring_bulk(a, mode, dtype, op, s);
+  } else {
+    const int lp = proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag;
+    const int64_t line_payload = lp == kLineWide && dtype != RINGSIM_INT64 ? 12 : 8;
+    e = max_unit_bytes(a, mode, esize) <= (int64_t)kThreads * line_payload
+            ? launch_ring_lines_one(a, lp, mode, dtype, op, s)
+            : launch_ring_lines_multi(a, lp, mode, dtype, op, s);
+  }
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "kernel launch failed: %s", hipGetErrorString(e));
     return RINGSIM_UNHANDLED_DEVICE_ERROR;
@@ -437,7 +453,8 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Bulk steps stage their own operand in LDS (double-buffered) unless the
   // slot is too large or RINGSIM_LDS_STAGE=0.
   const int lds_stage = cfg.slot_bytes <= (size_t)kMaxStagedSlotBytes && env_long("RINGSIM_LDS_STAGE", 1) != 0;
-  const int per_cu = std::min(bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_blocks_per_cu());
+  const int per_cu = std::min({bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_one_blocks_per_cu(),
+                               line_multi_blocks_per_cu()});
   if (per_cu <= 0) return RINGSIM_UNHANDLED_DEVICE_ERROR;
   const int64_t max_resident = (int64_t)per_cu * cus;
 

@@ -214,6 +214,19 @@ __device__ __forceinline__ bool give_up(const WaitCtx& w, uint64_t t0, uint32_t 
   return false;
 }
 
+// give_up() without memory side effects, for polling loops that must hold no
+// store (so that their loads retire in issue order): 0 = keep waiting,
+// kStopQuiet = stop (another workgroup already recorded an error), else the
+// error code the caller records once it has left the loop.
+constexpr uint32_t kStopQuiet = 0xffffffffu;
+__device__ __forceinline__ uint32_t wait_verdict(const WaitCtx& w, uint64_t t0, uint32_t it) {
+  if (it & 255u) return 0u;
+  if (dev_abort_seen(w)) return kStopQuiet;
+  if ((it & 16383u) == 0u && host_abort_seen(w)) return kErrAborted;
+  if (wall_clock64() - t0 > w.timeout_ticks) return kErrTimeout;
+  return 0u;
+}
+
 // Spins until *p >= target and returns the value seen, or returns 0 (never a
 // valid answer: targets start at 1) after recording why it gave up.
 __device__ __forceinline__ uint64_t wait_geq(const uint64_t* p, uint64_t target, WaitCtx w) {

@@ -105,16 +105,21 @@ struct CopyArgs {
   int vec_ok;
 };
 
-// Kernel launchers (ring_bulk.hip, ring_lines.hip, tree_flag.hip, copy.hip).
+// Kernel launchers (ring_bulk.hip, ring_lines_one.hip, ring_lines_multi.hip,
+// tree_flag.hip, copy.hip).
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
-hipError_t launch_ring_lines(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
+// Line protocols: the _one variant when no step of the launch holds more
+// than one line per thread, else _multi.
+hipError_t launch_ring_lines_one(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
+hipError_t launch_ring_lines_multi(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_tree_flag(const TreeArgs& a, int dtype, int op, hipStream_t s);
 // Max co-resident workgroups per CU over every instantiation of a kernel
 // family (the bulk kernels launched with `lds_bytes` of dynamic LDS).
 int tree_blocks_per_cu();
 int bulk_blocks_per_cu(size_t lds_bytes);
-int line_blocks_per_cu();
+int line_one_blocks_per_cu();
+int line_multi_blocks_per_cu();
 // Largest bulk slot that is staged in LDS (two buffers must fit beside a
 // second workgroup's on the 160 KiB of a CU).
 constexpr int kMaxStagedSlotBytes = 64 * 1024;
