@@ -34,9 +34,11 @@ struct RingModel {
   double wg_gbs[3] = {0.0, 11.5, 14.0};   // line protocols: per (rank, channel) workgroup
   double line_max_gbs = 4000.0;           // line protocols' ceiling
   double bulk_gbs = 6900.0;
-  // Double-binary tree (flag lines): per-hop latency and per-workgroup rate.
-  double tree_hop_us = 1.7;
-  double tree_wg_gbs = 13.0;
+  // Double-binary tree (flag lines): per-hop latency, per-workgroup rate of
+  // the ring-equivalent flag bytes, and the tree's ceiling.
+  double tree_hop_us = 1.33;
+  double tree_wg_gbs = 3.2;
+  double tree_max_gbs = 1800.0;
 };
 
 enum ModelColl : int { kModelAllReduce = 0, kModelReduceScatter = 1, kModelAllGather = 2 };
@@ -65,11 +67,13 @@ inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, 
 // Predicted microseconds of a double-binary-tree all-reduce: the reduce
 // climbs `depth` hops to each root and the broadcast descends as many, all
 // in flag-packed lines; the flag protocol's bytes move through the 4 x N x
-// tree_channels workgroups (two trees, an up and a down role each).
+// tree_channels workgroups (two trees, an up and a down role each), fitted to
+// the tree's own sweeps (16 and 8 ranks: ~1.33 us per hop, ~1.8 TB/s at
+// most).
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double bytes_per_rank) {
   if (nranks <= 1) return m.base_us;
   const double bytes = model_bytes(kModelAllReduce, nranks, bytes_per_rank, kModelFlag);
-  const double gbs = std::min(m.line_max_gbs, m.tree_wg_gbs * 4.0 * nranks * tree_channels);
+  const double gbs = std::min(m.tree_max_gbs, m.tree_wg_gbs * 4.0 * nranks * tree_channels);
   return m.base_us + 2.0 * depth * m.tree_hop_us + bytes / (gbs * 1e3);
 }
 

@@ -317,7 +317,11 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   a.host_abort = c->host_words_dev;
   a.host_err = c->host_words_dev + 1;
   a.timeout_ticks = c->timeout_ticks;
-  const hipError_t e = launch_tree_flag(a, dtype, op, s);
+  // The longest slice of the launch: tree 0 takes the larger half.
+  const int64_t A = 16 / dtype_size(dtype);
+  const int64_t longest = std::min<int64_t>(a.slot_bytes / 2, channel_span(tree_split(a.count, A), a.nchannels, A) *
+                                                                 dtype_size(dtype));
+  const hipError_t e = longest <= (int64_t)kThreads * 8 ? launch_tree_one(a, dtype, op, s) : launch_tree_multi(a, dtype, op, s);
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "tree kernel launch failed: %s", hipGetErrorString(e));
     return RINGSIM_UNHANDLED_DEVICE_ERROR;
@@ -479,7 +483,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
 
   // Tree channels: every workgroup of a tree launch (4 per rank and channel)
   // must be resident at once, like the ring's.
-  const int tree_per_cu = tree_blocks_per_cu();
+  const int tree_per_cu = std::min(tree_one_blocks_per_cu(), tree_multi_blocks_per_cu());
   const int64_t tree_resident = (int64_t)tree_per_cu * cus;
   const int tree_channels = nranks < 2 ? 0 : (int)std::min<int64_t>(nchannels, tree_resident / (4 * (int64_t)nranks));
   if (cfg.algo == RINGSIM_ALGO_TREE && nranks > 1 && tree_channels < 1) return RINGSIM_INVALID_USAGE;

@@ -106,17 +106,21 @@ struct CopyArgs {
 };
 
 // Kernel launchers (ring_bulk.hip, ring_lines_one.hip, ring_lines_multi.hip,
-// tree_flag.hip, copy.hip).
+// tree_one.hip, tree_multi.hip, copy.hip).
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 // Line protocols: the _one variant when no step of the launch holds more
 // than one line per thread, else _multi.
 hipError_t launch_ring_lines_one(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_lines_multi(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
-hipError_t launch_tree_flag(const TreeArgs& a, int dtype, int op, hipStream_t s);
+// Double-binary tree: the _one variant when no slice of the launch holds more
+// than one line per thread, else _multi.
+hipError_t launch_tree_one(const TreeArgs& a, int dtype, int op, hipStream_t s);
+hipError_t launch_tree_multi(const TreeArgs& a, int dtype, int op, hipStream_t s);
 // Max co-resident workgroups per CU over every instantiation of a kernel
 // family (the bulk kernels launched with `lds_bytes` of dynamic LDS).
-int tree_blocks_per_cu();
+int tree_one_blocks_per_cu();
+int tree_multi_blocks_per_cu();
 int bulk_blocks_per_cu(size_t lds_bytes);
 int line_one_blocks_per_cu();
 int line_multi_blocks_per_cu();

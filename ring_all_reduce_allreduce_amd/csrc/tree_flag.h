@@ -1,6 +1,8 @@
-// tree_flag.hip -- double-binary-tree all-reduce over flag-packed lines
+// tree_flag.h -- double-binary-tree all-reduce over flag-packed lines
 // ("NCCL" book, ch. 4: two binary trees, each reducing one half of the
 // buffer up to its root and broadcasting it back down).
+#pragma once
+
 #include "ringsim_device.h"
 #include "tree_plan.h"
 
@@ -11,12 +13,12 @@ namespace ringsim {
 // child), stored to each output FIFO under that FIFO's flag and to the
 // receive buffer. fin[j] / fout[j] (j < nin / nout) point at this step's
 // slots. Arrays are only ever indexed with unrolled constants.
-template <int DT, int OP>
+template <int DT, int OP, bool ONE>
 __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const char* lp, char* op, int nin,
                                            const uint64_t* const (&fin)[2], const uint32_t (&flag_in)[2],
                                            int nout, uint64_t* const (&fout)[2], const uint32_t (&flag_out)[2],
                                            int vec_ok, bool& stop, const WaitCtx& wc) {
-  if (nlines <= kThreads) {
+  if constexpr (ONE) {
     // At most one line per thread: the shortest path from a flag's arrival
     // to the next hop's store.
     const int li = threadIdx.x;
@@ -39,10 +41,10 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
       }
     }
     if (op) store_payload<DT>(op + (int64_t)li * 8, x, valid, vec_ok);
-    return;
-  }
+  } else {
   // Several lines per thread (lines tid, tid + 256, ...): issue every load
-  // first, then poll again only the lines whose flags are still missing.
+  // first, then poll again only the lines whose flags are still missing;
+  // every round issues all of its loads before it checks any of them.
   constexpr int U = kFlagLinesPerThread;
   u32x2 x[U];
   uint64_t v0[2][U], v1[2][U];
@@ -52,39 +54,62 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
     const int li = threadIdx.x + u * kThreads;
     x[u] = u32x2{0u, 0u};
     if (lp && li < nlines) x[u] = load_payload<DT>(lp + (int64_t)li * 8, (int)min64(8, nbytes - (int64_t)li * 8), vec_ok);
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int li = threadIdx.x + u * kThreads;
       v0[j][u] = v1[j][u] = 0;
       if (j < nin && li < nlines) {
         v0[j][u] = ld_relaxed(fin[j] + 2 * li);
         v1[j][u] = ld_relaxed(fin[j] + 2 * li + 1);
-        if ((uint32_t)(v0[j][u] >> 32) != flag_in[j] || (uint32_t)(v1[j][u] >> 32) != flag_in[j])
-          pending |= 1u << (j * U + u);
       }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j < nin && threadIdx.x + u * kThreads < nlines &&
+          ((uint32_t)(v0[j][u] >> 32) != flag_in[j] || (uint32_t)(v1[j][u] >> 32) != flag_in[j]))
+        pending |= 1u << (j * U + u);
     }
   }
   if (pending && !stop) {
     const uint64_t t0 = wall_clock64();
-    uint32_t spins = 0;
+    uint32_t spins = 0, verdict = 0;
     while (pending) {
-      if (give_up(wc, t0, ++spins)) {
-        stop = true;
-        break;
-      }
+      if ((verdict = wait_verdict(wc, t0, ++spins)) != 0u) break;
       __builtin_amdgcn_s_sleep(1);
+      uint64_t w0[2][U], w1[2][U];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (pending & (1u << (j * U + u))) {
             const int li = threadIdx.x + u * kThreads;
-            v0[j][u] = ld_relaxed(fin[j] + 2 * li);
-            v1[j][u] = ld_relaxed(fin[j] + 2 * li + 1);
-            if ((uint32_t)(v0[j][u] >> 32) == flag_in[j] && (uint32_t)(v1[j][u] >> 32) == flag_in[j])
-              pending &= ~(1u << (j * U + u));
+            w0[j][u] = ld_relaxed(fin[j] + 2 * li);
+            w1[j][u] = ld_relaxed(fin[j] + 2 * li + 1);
           }
         }
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t bit = 1u << (j * U + u);
+          if ((pending & bit) && (uint32_t)(w0[j][u] >> 32) == flag_in[j] && (uint32_t)(w1[j][u] >> 32) == flag_in[j]) {
+            v0[j][u] = w0[j][u];
+            v1[j][u] = w1[j][u];
+            pending &= ~bit;
+          }
+        }
+      }
+    }
+    if (verdict) {
+      stop = true;
+      if (verdict != kStopQuiet) raise_error(wc, verdict);
     }
   }
 #pragma unroll
@@ -108,6 +133,7 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
       if (op) store_payload<DT>(op + (int64_t)li * 8, x[u], (int)min64(8, nbytes - (int64_t)li * 8), vec_ok);
     }
   }
+  }
 }
 
 // One workgroup per (rank, tree, channel, role). Role 0 folds the rank's own
@@ -117,7 +143,9 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
 // it on to the children. Every FIFO carries one step per slice of the
 // channel; its producer owns `tail`, its consumer `head`, and a line's flag
 // is the low 32 bits of (step + 1).
-template <int DT, int OP>
+// ONE: the host has checked that no slice of this launch holds more than one
+// line per thread, so only the one-line path is compiled.
+template <int DT, int OP, bool ONE>
 __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int64_t E = sizeof(T);
@@ -244,7 +272,7 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
       flag_in[j] = (uint32_t)(in_base[j] + s + 1);
       flag_out[j] = (uint32_t)(out_base[j] + s + 1);
     }
-    tree_lines<DT, OP>(nlines, nbytes, own ? own + s * slice * E : nullptr, dst ? dst + s * slice * E : nullptr,
+    tree_lines<DT, OP, ONE>(nlines, nbytes, own ? own + s * slice * E : nullptr, dst ? dst + s * slice * E : nullptr,
                        nin, fin, flag_in, nout, fout, flag_out, a.vec_ok, stop, wc);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -270,50 +298,6 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
       if (j < nout) st_relaxed(&out_ctr[j]->tail, out_base[j] + nsl);
     }
   }
-}
-
-
-// ---------------------------------------------------------------------------
-// Host-side dispatch
-// ---------------------------------------------------------------------------
-
-template <int DT>
-static hipError_t tree_dispatch_op(const TreeArgs& a, int op, hipStream_t s) {
-  const int grid = a.nranks * 2 * a.nchannels * 2;
-  switch (op) {
-    case RINGSIM_SUM: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_SUM>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case RINGSIM_PROD: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_PROD>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case RINGSIM_MAX: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_MAX>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case RINGSIM_MIN: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_MIN>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_tree_flag(const TreeArgs& a, int dtype, int op, hipStream_t s) {
-  switch (dtype) {
-    case RINGSIM_INT32: return tree_dispatch_op<RINGSIM_INT32>(a, op, s);
-    case RINGSIM_INT64: return tree_dispatch_op<RINGSIM_INT64>(a, op, s);
-    case RINGSIM_FLOAT32: return tree_dispatch_op<RINGSIM_FLOAT32>(a, op, s);
-    case RINGSIM_BFLOAT16: return tree_dispatch_op<RINGSIM_BFLOAT16>(a, op, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-int tree_blocks_per_cu() {
-  int m = 1 << 30;
-  auto acc = [&](int v) { m = v < m ? v : m; };
-#define RS_TREE_OCC_DT(DT)                                    \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_SUM>, 0));       \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_PROD>, 0));      \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_MAX>, 0));       \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_MIN>, 0));
-  RS_TREE_OCC_DT(RINGSIM_INT32)
-  RS_TREE_OCC_DT(RINGSIM_INT64)
-  RS_TREE_OCC_DT(RINGSIM_FLOAT32)
-  RS_TREE_OCC_DT(RINGSIM_BFLOAT16)
-#undef RS_TREE_OCC_DT
-  return m == (1 << 30) ? 0 : m;
 }
 
 }  // namespace ringsim
