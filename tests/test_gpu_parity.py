@@ -297,3 +297,47 @@ def test_protocols_agree_across_groups_and_loops(dtype):
     for proto in ("bulk", "flag", "wide"):
         got = _run_allreduce(xs, dtype, "sum", nch, proto, chunk_bytes=chunk)
         _assert_same(got, want, dtype, f"{proto} {dtype} multi-group")
+
+
+@pytest.mark.parametrize("proto", ["flag", "wide"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int64"])
+def test_line_kernel_variant_boundary(proto, dtype):
+    """The host runs the one-line-per-thread kernel only when no unit of the
+    launch holds more than 256 lines (2 KiB of FLAG payload, 3 KiB of WIDE
+    payload, 2 KiB for int64 lines). Units of exactly that size and one
+    16-byte vector more take different kernels; both must be whole and
+    bit-exact, for the all-reduce, reduce-scatter and all-gather."""
+    e = {"float32": 4, "bfloat16": 2, "int64": 8}[dtype]
+    line_payload = 12 if proto == "wide" and dtype != "int64" else 8
+    limit = 256 * line_payload // e  # elements in the largest one-line unit
+    n = 4
+    for extra in (0, 16 // e):
+        unit = limit + extra
+        count = n * unit  # one tail loop per channel: chunk = unit
+        xs = _inputs(n, count, dtype, 1300 + unit)
+        got = _run_allreduce(xs, dtype, "sum", 1, proto)
+        want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=1)
+        _assert_same(got, want, dtype, f"allreduce {proto} unit={unit}")
+        # reduce-scatter / all-gather: one unit per loop of each block
+        for coll in ("reduce_scatter", "all_gather"):
+            comm = rs.comm_init(n, 1, proto, chunk_bytes=unit * e)
+            try:
+                if coll == "reduce_scatter":
+                    src = _inputs(n, n * unit, dtype, 1400 + unit)
+                    send = [G.to_device(x, dtype) for x in src]
+                    recv = [G.empty_like_rank(unit, dtype) for _ in range(n)]
+                    G.say(f"reduce_scatter {proto} {dtype} unit={unit}")
+                    rs.reduce_scatter(comm, send, recv, op="sum")
+                    want = oracle.ring_reduce_scatter(src, "sum", dtype, nchannels=1, chunk_bytes=unit * e)
+                else:
+                    src = _inputs(n, unit, dtype, 1500 + unit)
+                    send = [G.to_device(x, dtype) for x in src]
+                    recv = [G.empty_like_rank(n * unit, dtype) for _ in range(n)]
+                    G.say(f"all_gather {proto} {dtype} unit={unit}")
+                    rs.all_gather(comm, send, recv)
+                    want = oracle.ring_all_gather(src, dtype, nchannels=1, chunk_bytes=unit * e)
+                G.sync()
+                G.check_comm_ok(comm)
+                _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"{coll} {proto} unit={unit}")
+            finally:
+                rs.comm_destroy(comm)

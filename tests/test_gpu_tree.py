@@ -177,3 +177,24 @@ def test_tree_degenerate_shapes():
             _assert_tree(got, xs, "float32", "sum", f"count={count}")
     finally:
         rs.comm_destroy(comm)
+
+
+@pytest.mark.parametrize("dtype", ["int32", "bfloat16", "int64"])
+def test_tree_kernel_variant_boundary(dtype):
+    """The host runs the tree's one-line-per-thread kernel only when no slice
+    holds more than 256 lines (2 KiB of payload). Tree 0 takes the larger
+    half; halves of exactly 2 KiB and of one 16-byte vector more take
+    different kernels, and both must be whole and bit-exact."""
+    e = {"int32": 4, "bfloat16": 2, "int64": 8}[dtype]
+    half = 2048 // e
+    n = 8
+    comm = rs.comm_init(n, 4, "auto", algo="tree")
+    try:
+        for extra in (0, 16 // e):
+            count = 2 * (half + extra)
+            xs = _inputs(n, count, dtype, 1600 + count)
+            G.say(f"tree boundary {dtype} count={count}")
+            got = _run(comm, xs, dtype, "sum")
+            _assert_tree(got, xs, dtype, "sum", f"tree boundary count={count}")
+    finally:
+        rs.comm_destroy(comm)
