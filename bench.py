@@ -168,26 +168,29 @@ def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 20.0) -> di
     }
 
 
-def d2d_copy_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
-    """Device-to-device copy (read + write bytes / time) as the
-    achievable-bandwidth context of this box: 1 GiB streams from HBM; 128 MiB
-    (source and destination both fit in the 256 MB Infinity Cache) is the
-    ceiling for traffic that the cache serves, as the FIFO slots are."""
+def d2d_copy_gbs(nbytes: int = 1 << 30, reps: int = 10, trials: int = 5) -> float:
+    """Device-to-device copy (read + write bytes / time, median of `trials`
+    batches of `reps` copies) as the achievable-bandwidth context of this box:
+    1 GiB streams from HBM; 64 MiB (source and destination both fit in the
+    256 MB Infinity Cache) is the ceiling for traffic that the cache serves,
+    as the FIFO slots are."""
     import torch
 
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     b.copy_(a)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / reps
+    rates = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(2 * nbytes / (e0.elapsed_time(e1) / 1e3 / reps) / 1e9)
     del a, b
-    return 2 * nbytes / t / 1e9
+    return statistics.median(rates)
 
 
 def copy_calibration(args) -> int:
@@ -407,7 +410,7 @@ def main() -> int:
     src_hash = kernel_source_hash()
     traffic = load_traffic(args.workload, src_hash)
     d2d = d2d_copy_gbs()
-    cache_copy = d2d_copy_gbs(128 << 20, reps=50)
+    cache_copy = d2d_copy_gbs(64 << 20, reps=50)
     log(f"[bench] per-launch median {t_med * 1e6:.1f} us, avg {t_avg * 1e6:.1f} us, p95 {t_p95 * 1e6:.1f} us, "
         f"CV {cv * 100:.2f}%  algBW {algbw:.1f} GB/s busBW {busbw:.1f} GB/s  "
         f"alg-bytes rate {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)  "
