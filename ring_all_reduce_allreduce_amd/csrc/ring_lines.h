@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   uint32_t out_slot = (uint32_t)(out_base % nslots);
 
   const int64_t slice = (int64_t)(a.slot_bytes / 16) * F::PB / E;  // payload elements per slot
-  StepIter<DT, MODE> it;
+  StepIter<DT, MODE, true> it;  // the line protocols run one workgroup per channel
   it.init(a, p.r, p.c, p.w, slice, (int64_t)a.group * slice);
   for (; !it.done; it.next()) {
     const bool recv = it.recv, send = it.send;

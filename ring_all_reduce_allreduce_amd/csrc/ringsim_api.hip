@@ -220,7 +220,7 @@ int model_proto(int proto) {
 void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize) {
   a->chunk = (int64_t)c->chunk_bytes / esize;
   if (proto == RINGSIM_PROTO_FLAG || proto == RINGSIM_PROTO_WIDE) {
-    a->wpc = 1;
+    a->wpc = 1;  // the line kernels walk whole chunks: one workgroup per (rank, channel)
     a->fifo = c->flag_fifo;
     a->fifo_stride = c->nchannels;
     a->fifo_mul = 1;

@@ -290,7 +290,10 @@ __device__ __forceinline__ Pipe locate(const RingArgs& a) {
 // rank r produced, group by group), and a step still reduces the same
 // elements in the same rank order, so values do not change; but a stage puts
 // at most one group into the FIFO, whatever the chunk size.
-template <int DT, int MODE>
+// ONE_WG: one workgroup per channel (wpc == 1, the line protocols), so a
+// unit is a whole chunk or block slice and no part split (no division) is
+// needed per unit.
+template <int DT, int MODE, bool ONE_WG = false>
 struct StepIter {
   static constexpr int64_t E = sizeof(typename Elem<DT>::T);
   static constexpr int64_t A = 16 / E;
@@ -318,13 +321,18 @@ struct StepIter {
     rem = L - off;
     if constexpr (MODE == kAllReduce) {
       cur = ar_loop_chunk(rem, N, chunk, A);
-      sub_full = align_up(div_up(cur, wpc), A);
+      sub_full = ONE_WG ? cur : align_up(div_up(cur, wpc), A);
       umax = sub_full;
     } else {
       cur = min64(chunk, rem);
-      const Range pt = split_part(cur, wpc, w, A);
-      part_lo = pt.lo;
-      part_n = pt.hi - pt.lo;
+      if constexpr (ONE_WG) {
+        part_lo = 0;
+        part_n = cur;
+      } else {
+        const Range pt = split_part(cur, wpc, w, A);
+        part_lo = pt.lo;
+        part_n = pt.hi - pt.lo;
+      }
       umax = part_n;
     }
     g_lo = 0;
@@ -342,10 +350,15 @@ struct StepIter {
     if constexpr (MODE == kAllReduce) {
       const int64_t clo = min64((int64_t)idx * cur, rem);
       const int64_t n = min64(clo + cur, rem) - clo;
-      const int64_t sub = n == cur ? sub_full : align_up(div_up(n, wpc), A);
-      const int64_t plo = min64((int64_t)w * sub, n);
-      m = min64(plo + sub, n) - plo;
-      local_e = out_e = ch_lo + off + clo + plo;
+      if constexpr (ONE_WG) {
+        m = n;
+        local_e = out_e = ch_lo + off + clo;
+      } else {
+        const int64_t sub = n == cur ? sub_full : align_up(div_up(n, wpc), A);
+        const int64_t plo = min64((int64_t)w * sub, n);
+        m = min64(plo + sub, n) - plo;
+        local_e = out_e = ch_lo + off + clo + plo;
+      }
       recv = j >= 1;
       use_local = j <= N - 1;
       send = j <= 2 * N - 3;
