@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   const Pipe p = locate(a);
   if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
   __shared__ uint64_t s_base[2];
-  __shared__ uint64_t s_head;
+  __shared__ int s_credit;
   if (threadIdx.x == 0) {
     s_base[0] = ld_relaxed(&p.in_ctr->head);
     s_base[1] = ld_relaxed(&p.out_ctr->tail);
@@ -177,37 +177,42 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   __syncthreads();
   const uint64_t in_base = s_base[0];
   const uint64_t out_base = s_base[1];
-  const uint64_t nslots = (uint64_t)a.nslots;
-  uint64_t nrecv = 0, nsent = 0;
-  uint64_t head_known = out_base;  // uniform across the workgroup
-  uint64_t known_head = 0;         // thread 0
-  bool stop = false;               // per thread: stop waiting
+  const int nslots = a.nslots;
+  // Per-call step counts and flags are 32-bit (a call moves far fewer than
+  // 2^32 steps; flags are the low 32 bits of the 64-bit counters anyway), so
+  // the per-step bookkeeping stays in scalar 32-bit arithmetic.
+  uint32_t nrecv = 0, nsent = 0;
+  const uint32_t in_base32 = (uint32_t)in_base, out_base32 = (uint32_t)out_base;
+  // Sends allowed before the consumer's head must be read again (uniform).
+  // Both counters of a FIFO are equal when a call starts, so all slots are free.
+  int credit = nslots;
+  bool stop = false;  // per thread: stop waiting
   const WaitCtx wc = wait_ctx(a);
-  uint32_t in_slot = (uint32_t)(in_base % nslots);
-  uint32_t out_slot = (uint32_t)(out_base % nslots);
+  uint32_t in_slot = (uint32_t)(in_base % (uint64_t)nslots);
+  uint32_t out_slot = (uint32_t)(out_base % (uint64_t)nslots);
 
   const int64_t slice = (int64_t)(a.slot_bytes / 16) * F::PB / E;  // payload elements per slot
   StepIter<DT, MODE, true> it;  // the line protocols run one workgroup per channel
   it.init(a, p.r, p.c, p.w, slice, (int64_t)a.group * slice);
   for (; !it.done; it.next()) {
     const bool recv = it.recv, send = it.send;
-    if (send && nsent + 1 > nslots) {
-      const uint64_t need = out_base + nsent + 1 - nslots;
-      if (head_known < need) {  // uniform branch
-        if (threadIdx.x == 0) {
-          if (!stop && known_head < need) {
-            known_head = wait_geq(&p.out_ctr->head, need, wc);
-            stop = known_head == 0;
-          }
-          s_head = known_head > need ? known_head : need;
+    if (send && credit == 0) {  // uniform branch: wait until step nsent - nslots is drained
+      if (threadIdx.x == 0) {
+        const uint64_t need = out_base + nsent + 1 - (uint64_t)nslots;
+        uint64_t h = need;
+        if (!stop) {
+          const uint64_t seen = wait_geq(&p.out_ctr->head, need, wc);
+          stop = seen == 0;
+          if (seen) h = seen;
         }
-        __syncthreads();
-        head_known = s_head;
-        __syncthreads();
+        s_credit = (int)(h + (uint64_t)nslots - (out_base + nsent));
       }
+      __syncthreads();
+      credit = s_credit;
+      __syncthreads();
     }
-    const uint32_t flag_in = (uint32_t)(in_base + nrecv + 1);
-    const uint32_t flag_out = (uint32_t)(out_base + nsent + 1);
+    const uint32_t flag_in = in_base32 + nrecv + 1;
+    const uint32_t flag_out = out_base32 + nsent + 1;
     Slot<LP> fin, fout;
     fin.init(recv ? p.in_fifo + (int64_t)in_slot * a.slot_bytes : nullptr, a.slot_bytes);
     fout.init(send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr, a.slot_bytes);
@@ -327,6 +332,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
     }
     if (send) {
       ++nsent;
+      --credit;
       out_slot = out_slot + 1 == (uint32_t)nslots ? 0 : out_slot + 1;
     }
   }

@@ -300,14 +300,19 @@ struct StepIter {
   // fixed per workgroup
   const char* send_r;
   char* recv_r;
-  int64_t count, chunk, L, ch_lo, slice;
+  int64_t count, chunk, L, ch_lo;
+  int slice;  // elements per step (a slot's payload)
   int N, r, w, wpc;
   // loop, group and stage
   int64_t off, rem, cur, sub_full, part_lo, part_n;
-  int64_t glen, g_lo, umax;  // group length, start of the current group, longest unit of the loop
+  int glen, g_lo, umax;  // group length, start of the current group, longest unit of the loop
   int j, idx;
   // current unit and step
-  int64_t m, s, s_end, local_e, out_e;
+  int64_t local_e, out_e;
+  // unit length, current step inside it, end of its steps in this group;
+  // 32-bit (a unit is at most one chunk, < 2^30 elements) to keep the
+  // per-step bookkeeping in scalar 32-bit arithmetic
+  int m, s, s_end;
   bool recv, use_local, send, store, done;
 
   __device__ __forceinline__ int nstages() const { return MODE == kAllReduce ? 2 * N - 1 : N; }
@@ -322,7 +327,7 @@ struct StepIter {
     if constexpr (MODE == kAllReduce) {
       cur = ar_loop_chunk(rem, N, chunk, A);
       sub_full = ONE_WG ? cur : align_up(div_up(cur, wpc), A);
-      umax = sub_full;
+      umax = (int)sub_full;
     } else {
       cur = min64(chunk, rem);
       if constexpr (ONE_WG) {
@@ -333,7 +338,7 @@ struct StepIter {
         part_lo = pt.lo;
         part_n = pt.hi - pt.lo;
       }
-      umax = part_n;
+      umax = (int)part_n;
     }
     g_lo = 0;
     begin_group();
@@ -343,7 +348,7 @@ struct StepIter {
   __device__ __forceinline__ void set_unit() {
     set_unit_range();
     s = g_lo;
-    s_end = min64(m, g_lo + glen);
+    s_end = m - g_lo < glen ? m : g_lo + glen;
   }
 
   __device__ __forceinline__ void set_unit_range() {
@@ -351,12 +356,12 @@ struct StepIter {
       const int64_t clo = min64((int64_t)idx * cur, rem);
       const int64_t n = min64(clo + cur, rem) - clo;
       if constexpr (ONE_WG) {
-        m = n;
+        m = (int)n;
         local_e = out_e = ch_lo + off + clo;
       } else {
         const int64_t sub = n == cur ? sub_full : align_up(div_up(n, wpc), A);
         const int64_t plo = min64((int64_t)w * sub, n);
-        m = min64(plo + sub, n) - plo;
+        m = (int)(min64(plo + sub, n) - plo);
         local_e = out_e = ch_lo + off + clo + plo;
       }
       recv = j >= 1;
@@ -364,7 +369,7 @@ struct StepIter {
       send = j <= 2 * N - 3;
       store = j >= N - 1;
     } else if constexpr (MODE == kReduceScatter) {
-      m = part_n;
+      m = (int)part_n;
       out_e = ch_lo + off + part_lo;
       local_e = (int64_t)idx * count + out_e;
       recv = j >= 1;
@@ -372,7 +377,7 @@ struct StepIter {
       send = j <= N - 2;
       store = j == N - 1;
     } else {
-      m = part_n;
+      m = (int)part_n;
       local_e = ch_lo + off + part_lo;
       out_e = (int64_t)idx * count + local_e;
       recv = j >= 1;
@@ -389,8 +394,8 @@ struct StepIter {
       ++j;
       idx = idx == 0 ? N - 1 : idx - 1;
       if (j == nstages()) {
-        g_lo += glen;
-        if (g_lo < umax) {
+        if (umax - g_lo > glen) {
+          g_lo += glen;
           begin_group();
         } else {
           off += MODE == kAllReduce ? (int64_t)N * chunk : chunk;
@@ -415,8 +420,8 @@ struct StepIter {
     wpc = a.wpc;
     count = a.count;
     chunk = a.chunk;
-    slice = slice_elems;
-    glen = group_elems > 0 ? group_elems : ((int64_t)1 << 60);
+    slice = (int)slice_elems;
+    glen = group_elems > 0 ? (int)group_elems : 0x7fffffff;
     send_r = a.send[r];
     recv_r = a.recv[r];
     const Range ch = channel_range(a.count, a.nchannels, c, A);
@@ -436,7 +441,7 @@ struct StepIter {
     next_unit();
   }
 
-  __device__ __forceinline__ int64_t ns() const { return min64(slice, s_end - s); }
+  __device__ __forceinline__ int64_t ns() const { return slice < s_end - s ? slice : s_end - s; }
   __device__ __forceinline__ const char* local() const { return send_r + (local_e + s) * E; }
   __device__ __forceinline__ char* out() const { return recv_r + (out_e + s) * E; }
 };
