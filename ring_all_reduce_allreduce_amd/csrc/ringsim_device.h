@@ -306,6 +306,8 @@ struct StepIter {
   // loop, group and stage
   int64_t off, rem, cur, sub_full, part_lo, part_n;
   int glen, g_lo, umax;  // group length, start of the current group, longest unit of the loop
+  int kfull;             // all-reduce, one workgroup per channel: chunks of the loop that are whole
+  int64_t tail;          // ... and the length of chunk kfull (the ragged one, possibly 0)
   int j, idx;
   // current unit and step
   int64_t local_e, out_e;
@@ -328,6 +330,12 @@ struct StepIter {
       cur = ar_loop_chunk(rem, N, chunk, A);
       sub_full = ONE_WG ? cur : align_up(div_up(cur, wpc), A);
       umax = (int)sub_full;
+      if constexpr (ONE_WG) {
+        // One division per loop instead of 64-bit clamps per unit: chunk k
+        // is whole for k < kfull, `tail` long for k == kfull, empty beyond.
+        kfull = rem >= (int64_t)N * cur ? N : (int)(rem / cur);
+        tail = kfull < N ? rem - (int64_t)kfull * cur : 0;
+      }
     } else {
       cur = min64(chunk, rem);
       if constexpr (ONE_WG) {
@@ -353,12 +361,12 @@ struct StepIter {
 
   __device__ __forceinline__ void set_unit_range() {
     if constexpr (MODE == kAllReduce) {
-      const int64_t clo = min64((int64_t)idx * cur, rem);
-      const int64_t n = min64(clo + cur, rem) - clo;
       if constexpr (ONE_WG) {
-        m = (int)n;
-        local_e = out_e = ch_lo + off + clo;
+        m = idx < kfull ? (int)cur : (idx == kfull ? (int)tail : 0);
+        local_e = out_e = ch_lo + off + (int64_t)idx * cur;
       } else {
+        const int64_t clo = min64((int64_t)idx * cur, rem);
+        const int64_t n = min64(clo + cur, rem) - clo;
         const int64_t sub = n == cur ? sub_full : align_up(div_up(n, wpc), A);
         const int64_t plo = min64((int64_t)w * sub, n);
         m = (int)(min64(plo + sub, n) - plo);
