@@ -14,8 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libringsim.so")
-SOURCES = ["ringsim_api.hip", "ring_bulk.hip", "ring_lines_one.hip", "ring_lines_multi.hip", "tree_one.hip",
-           "tree_multi.hip", "copy.hip"]
+SOURCES = ["ringsim_api.hip", "ring_bulk.hip", "ring_lines_half.hip", "ring_lines_one.hip", "ring_lines_multi.hip",
+           "tree_one.hip", "tree_multi.hip", "copy.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.

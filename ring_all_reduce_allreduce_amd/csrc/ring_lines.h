@@ -157,10 +157,20 @@ __device__ __forceinline__ u32x4 reduce_payload(u32x4 a, u32x4 b) {
 
 }  // namespace
 
-// ONE: the host has checked that no step of this launch holds more than one
-// line per thread, so only the one-line path is compiled; otherwise every
-// step takes the several-lines path.
-template <int LP, bool ONE, int DT, int OP, int MODE>
+// Line modes: how the lines of a step map onto the 256 threads.
+//   kLinesHalf  the host has checked that no step holds more than 128 lines:
+//               consecutive steps alternate between the two halves of the
+//               workgroup, one line per thread. A wave's loads and stores
+//               share one counter (vmcnt), and a wave that reads a load's
+//               result while its own stores are in flight waits for those
+//               stores too; alternating halves lets one step's store
+//               acknowledgements drain while the other half polls the next
+//               step, which took ~20% off every hop on MI355X.
+//   kLinesOne   at most 256 lines per step: every thread one line.
+//   kLinesMulti any step (up to 4 lines per thread).
+enum LineMode : int { kLinesMulti = 0, kLinesOne = 1, kLinesHalf = 2 };
+
+template <int LP, int LM, int DT, int OP, int MODE>
 __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
   using F = LineFmt<LP, DT>;
@@ -181,7 +191,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   // Per-call step counts and flags are 32-bit (a call moves far fewer than
   // 2^32 steps; flags are the low 32 bits of the 64-bit counters anyway), so
   // the per-step bookkeeping stays in scalar 32-bit arithmetic.
-  uint32_t nrecv = 0, nsent = 0;
+  uint32_t nrecv = 0, nsent = 0, nstep = 0;
   const uint32_t in_base32 = (uint32_t)in_base, out_base32 = (uint32_t)out_base;
   // Sends allowed before the consumer's head must be read again (uniform).
   // Both counters of a FIFO are equal when a call starts, so all slots are free.
@@ -221,11 +231,11 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
     const char* lp = it.use_local ? it.local() : nullptr;
     char* up = it.store ? it.out() : nullptr;
     const rsrc_t ur = make_rsrc(up, up ? nbytes : 0);
-    if constexpr (ONE) {
+    if constexpr (LM != kLinesMulti) {
       // At most one line per thread (small messages): the shortest path from
       // a flag's arrival to the next hop's store.
-      const int li = threadIdx.x;
-      if (li < nlines) {
+      const int li = LM == kLinesHalf ? (int)threadIdx.x - (int)(nstep & 1u) * (kThreads / 2) : (int)threadIdx.x;
+      if (li >= 0 && li < nlines && (LM != kLinesHalf || li < kThreads / 2)) {
         const int valid = (int)min64(F::PB, nbytes - (int64_t)li * F::PB);
         u32x4 loc = u32x4{0u, 0u, 0u, 0u};
         if (lp) loc = load_user<DT, F::PD>(lp + (int64_t)li * F::PB, valid, a.vec_ok);
@@ -330,6 +340,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
         if (threadIdx.x == 0) st_relaxed(&p.in_ctr->head, in_base + nrecv);
       }
     }
+    ++nstep;
     if (send) {
       ++nsent;
       --credit;

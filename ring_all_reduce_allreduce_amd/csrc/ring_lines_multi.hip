@@ -12,7 +12,7 @@ struct LineLaunch {
   template <int DT, int OP, int MODE>
   static hipError_t run(const RingArgs& a, hipStream_t s) {
     const int grid = a.nranks * a.nchannels * a.wpc;
-    hipLaunchKernelGGL((ring_line_kernel<LP, false, DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((ring_line_kernel<LP, kLinesMulti, DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
 };
@@ -28,9 +28,9 @@ int line_multi_blocks_per_cu() {
   int m = 1 << 30;
   auto acc = [&](int v) { m = v < m ? v : m; };
 #define RS_OCC_LINE(LP, DT)                                                           \
-  acc(occupancy(ring_line_kernel<LP, false, DT, RINGSIM_SUM, kAllReduce>, 0));      \
-  acc(occupancy(ring_line_kernel<LP, false, DT, RINGSIM_MIN, kReduceScatter>, 0));  \
-  acc(occupancy(ring_line_kernel<LP, false, DT, RINGSIM_SUM, kAllGather>, 0));
+  acc(occupancy(ring_line_kernel<LP, kLinesMulti, DT, RINGSIM_SUM, kAllReduce>, 0));      \
+  acc(occupancy(ring_line_kernel<LP, kLinesMulti, DT, RINGSIM_MIN, kReduceScatter>, 0));  \
+  acc(occupancy(ring_line_kernel<LP, kLinesMulti, DT, RINGSIM_SUM, kAllGather>, 0));
   RS_OCC_LINE(kLineFlag, RINGSIM_INT32)
   RS_OCC_LINE(kLineFlag, RINGSIM_INT64)
   RS_OCC_LINE(kLineFlag, RINGSIM_FLOAT32)

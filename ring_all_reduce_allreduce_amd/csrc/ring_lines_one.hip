@@ -1,5 +1,5 @@
 // ring_lines_one.hip -- instantiations of the line-protocol ring kernel for
-// steps of at most one line per thread (small messages).
+// steps of at most one line per thread (256 lines).
 #include "ring_lines.h"
 
 namespace ringsim {
@@ -12,7 +12,7 @@ struct LineLaunch {
   template <int DT, int OP, int MODE>
   static hipError_t run(const RingArgs& a, hipStream_t s) {
     const int grid = a.nranks * a.nchannels * a.wpc;
-    hipLaunchKernelGGL((ring_line_kernel<LP, true, DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((ring_line_kernel<LP, kLinesOne, DT, OP, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
 };
@@ -28,9 +28,9 @@ int line_one_blocks_per_cu() {
   int m = 1 << 30;
   auto acc = [&](int v) { m = v < m ? v : m; };
 #define RS_OCC_LINE(LP, DT)                                                           \
-  acc(occupancy(ring_line_kernel<LP, true, DT, RINGSIM_SUM, kAllReduce>, 0));      \
-  acc(occupancy(ring_line_kernel<LP, true, DT, RINGSIM_MIN, kReduceScatter>, 0));  \
-  acc(occupancy(ring_line_kernel<LP, true, DT, RINGSIM_SUM, kAllGather>, 0));
+  acc(occupancy(ring_line_kernel<LP, kLinesOne, DT, RINGSIM_SUM, kAllReduce>, 0));      \
+  acc(occupancy(ring_line_kernel<LP, kLinesOne, DT, RINGSIM_MIN, kReduceScatter>, 0));  \
+  acc(occupancy(ring_line_kernel<LP, kLinesOne, DT, RINGSIM_SUM, kAllGather>, 0));
   RS_OCC_LINE(kLineFlag, RINGSIM_INT32)
   RS_OCC_LINE(kLineFlag, RINGSIM_INT64)
   RS_OCC_LINE(kLineFlag, RINGSIM_FLOAT32)

@@ -15,7 +15,7 @@
 // line format: x2 for the flag protocol's 8-of-16-byte lines, x4/3 for the
 // wide protocol's 12-of-16), and constants fitted to bench.py --sweep on
 // MI355X (16 and 8 ranks and channels, 8 B .. 64 MiB per rank): a hop costs
-// ~1.23 us (flag), ~1.4 us (wide) or ~2.45 us (bulk) when every chunk of
+// ~1.0 us (flag), ~1.1 us (wide) or ~2.45 us (bulk) when every chunk of
 // the ring is busy; one line-protocol workgroup sustains ~11.5 (flag) or
 // ~14 (wide) GB/s of method bytes, the bulk kernel ~6.9 TB/s in total.
 #pragma once
@@ -30,7 +30,7 @@ enum ModelProto : int { kModelBulk = 0, kModelFlag = 1, kModelWide = 2 };
 
 struct RingModel {
   double base_us = 3.0;
-  double hop_us[3] = {2.45, 1.23, 1.4};  // bulk, flag, wide
+  double hop_us[3] = {2.45, 1.0, 1.1};  // bulk, flag, wide
   double wg_gbs[3] = {0.0, 11.5, 14.0};   // line protocols: per (rank, channel) workgroup
   double line_max_gbs = 4000.0;           // line protocols' ceiling
   double bulk_gbs = 6900.0;

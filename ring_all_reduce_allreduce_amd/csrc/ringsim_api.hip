@@ -372,9 +372,10 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   } else {
     const int lp = proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag;
     const int64_t line_payload = lp == kLineWide && dtype != RINGSIM_INT64 ? 12 : 8;
-    e = max_unit_bytes(a, mode, esize) <= (int64_t)kThreads * line_payload
-            ? launch_ring_lines_one(a, lp, mode, dtype, op, s)
-            : launch_ring_lines_multi(a, lp, mode, dtype, op, s);
+    const int64_t unit = max_unit_bytes(a, mode, esize);
+    e = unit <= (int64_t)(kThreads / 2) * line_payload ? launch_ring_lines_half(a, lp, mode, dtype, op, s)
+        : unit <= (int64_t)kThreads * line_payload     ? launch_ring_lines_one(a, lp, mode, dtype, op, s)
+                                                       : launch_ring_lines_multi(a, lp, mode, dtype, op, s);
   }
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "kernel launch failed: %s", hipGetErrorString(e));
@@ -457,8 +458,8 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Bulk steps stage their own operand in LDS (double-buffered) unless the
   // slot is too large or RINGSIM_LDS_STAGE=0.
   const int lds_stage = cfg.slot_bytes <= (size_t)kMaxStagedSlotBytes && env_long("RINGSIM_LDS_STAGE", 1) != 0;
-  const int per_cu = std::min({bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_one_blocks_per_cu(),
-                               line_multi_blocks_per_cu()});
+  const int per_cu = std::min({bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_half_blocks_per_cu(),
+                               line_one_blocks_per_cu(), line_multi_blocks_per_cu()});
   if (per_cu <= 0) return RINGSIM_UNHANDLED_DEVICE_ERROR;
   const int64_t max_resident = (int64_t)per_cu * cus;
 

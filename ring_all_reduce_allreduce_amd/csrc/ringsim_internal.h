@@ -105,11 +105,12 @@ struct CopyArgs {
   int vec_ok;
 };
 
-// Kernel launchers (ring_bulk.hip, ring_lines_one.hip, ring_lines_multi.hip,
-// tree_one.hip, tree_multi.hip, copy.hip).
+// Kernel launchers (ring_bulk.hip, ring_lines_half.hip, ring_lines_one.hip,
+// ring_lines_multi.hip, tree_one.hip, tree_multi.hip, copy.hip).
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
-// Line protocols: the _one variant when no step of the launch holds more
-// than one line per thread, else _multi.
+// Line protocols: the _half variant when no step of the launch holds more
+// than 128 lines, _one when none holds more than 256, else _multi.
+hipError_t launch_ring_lines_half(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_lines_one(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_lines_multi(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
@@ -122,6 +123,7 @@ hipError_t launch_tree_multi(const TreeArgs& a, int dtype, int op, hipStream_t s
 int tree_one_blocks_per_cu();
 int tree_multi_blocks_per_cu();
 int bulk_blocks_per_cu(size_t lds_bytes);
+int line_half_blocks_per_cu();
 int line_one_blocks_per_cu();
 int line_multi_blocks_per_cu();
 // Largest bulk slot that is staged in LDS (two buffers must fit beside a

@@ -302,17 +302,17 @@ def test_protocols_agree_across_groups_and_loops(dtype):
 @pytest.mark.parametrize("proto", ["flag", "wide"])
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int64"])
 def test_line_kernel_variant_boundary(proto, dtype):
-    """The host runs the one-line-per-thread kernel only when no unit of the
-    launch holds more than 256 lines (2 KiB of FLAG payload, 3 KiB of WIDE
-    payload, 2 KiB for int64 lines). Units of exactly that size and one
-    16-byte vector more take different kernels; both must be whole and
+    """The host runs the alternating-halves kernel when no unit of the launch
+    holds more than 128 lines, the one-line-per-thread kernel up to 256
+    lines (2 KiB of FLAG payload, 3 KiB of WIDE payload, 2 KiB for int64
+    lines) and the several-lines kernel above. Units of exactly each limit
+    and one 16-byte vector more take different kernels; all must be whole and
     bit-exact, for the all-reduce, reduce-scatter and all-gather."""
     e = {"float32": 4, "bfloat16": 2, "int64": 8}[dtype]
     line_payload = 12 if proto == "wide" and dtype != "int64" else 8
-    limit = 256 * line_payload // e  # elements in the largest one-line unit
     n = 4
-    for extra in (0, 16 // e):
-        unit = limit + extra
+    for lines, extra in ((128, 0), (128, 16 // e), (256, 0), (256, 16 // e)):
+        unit = lines * line_payload // e + extra
         count = n * unit  # one tail loop per channel: chunk = unit
         xs = _inputs(n, count, dtype, 1300 + unit)
         got = _run_allreduce(xs, dtype, "sum", 1, proto)
