@@ -36,7 +36,7 @@ struct RingModel {
   double bulk_gbs = 6900.0;
   // Double-binary tree (flag lines): per-hop latency, per-workgroup rate of
   // the ring-equivalent flag bytes, and the tree's ceiling.
-  double tree_hop_us = 1.33;
+  double tree_hop_us = 1.25;
   double tree_wg_gbs = 3.2;
   double tree_max_gbs = 1800.0;
 };
@@ -68,7 +68,7 @@ inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, 
 // climbs `depth` hops to each root and the broadcast descends as many, all
 // in flag-packed lines; the flag protocol's bytes move through the 4 x N x
 // tree_channels workgroups (two trees, an up and a down role each), fitted to
-// the tree's own sweeps (16 and 8 ranks: ~1.33 us per hop, ~1.8 TB/s at
+// the tree's own sweeps (16 and 8 ranks: ~1.25 us per hop, ~1.8 TB/s at
 // most).
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double bytes_per_rank) {
   if (nranks <= 1) return m.base_us;

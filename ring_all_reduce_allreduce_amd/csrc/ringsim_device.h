@@ -458,29 +458,6 @@ struct StepIter {
 // Flag-packed lines (8-byte words of {4-byte payload, 4-byte flag})
 // ---------------------------------------------------------------------------
 
-// Flag-packed FIFO line: 16 bytes {payload word 0, flag, payload word 1,
-// flag}; each 8-byte half is written and read as one 64-bit access, so a
-// matching flag vouches for the word stored with it. Polls until both flags
-// equal `flag` (or the wait is abandoned) and returns the two payload words.
-__device__ __forceinline__ u32x2 poll_line(const uint64_t* line, uint32_t flag, bool& stop, const WaitCtx& w) {
-  uint64_t v0 = ld_relaxed(line);
-  uint64_t v1 = ld_relaxed(line + 1);
-  if (!stop && ((uint32_t)(v0 >> 32) != flag || (uint32_t)(v1 >> 32) != flag)) {
-    const uint64_t t0 = wall_clock64();
-    uint32_t it = 0;
-    while ((uint32_t)(v0 >> 32) != flag || (uint32_t)(v1 >> 32) != flag) {
-      if (give_up(w, t0, ++it)) {
-        stop = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-      v0 = ld_relaxed(line);
-      v1 = ld_relaxed(line + 1);
-    }
-  }
-  return u32x2{(uint32_t)v0, (uint32_t)v1};
-}
-
 template <int DT>
 __device__ __forceinline__ u32x2 load_payload(const char* p, int valid, int vec_ok) {
   using T = typename Elem<DT>::T;

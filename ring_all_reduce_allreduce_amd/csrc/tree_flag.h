@@ -26,10 +26,53 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
     const int valid = (int)min64(8, nbytes - (int64_t)li * 8);
     u32x2 x = u32x2{0u, 0u};
     if (lp) x = load_payload<DT>(lp + (int64_t)li * 8, valid, vec_ok);
+    // Both children's lines are polled together: loads of both go out
+    // before either is checked, and a round re-reads only what is missing.
+    uint64_t v0[2] = {0, 0}, v1[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (j < nin) {
-        const u32x2 y = poll_line(fin[j] + 2 * li, flag_in[j], stop, wc);
+        v0[j] = ld_relaxed(fin[j] + 2 * li);
+        v1[j] = ld_relaxed(fin[j] + 2 * li + 1);
+      }
+    }
+    uint32_t pending = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < nin && ((uint32_t)(v0[j] >> 32) != flag_in[j] || (uint32_t)(v1[j] >> 32) != flag_in[j]))
+        pending |= 1u << j;
+    if (pending && !stop) {
+      const uint64_t t0 = wall_clock64();
+      uint32_t spins = 0, verdict = 0;
+      while (pending) {
+        if ((verdict = wait_verdict(wc, t0, ++spins)) != 0u) break;
+        __builtin_amdgcn_s_sleep(1);
+        uint64_t w0[2], w1[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (pending & (1u << j)) {
+            w0[j] = ld_relaxed(fin[j] + 2 * li);
+            w1[j] = ld_relaxed(fin[j] + 2 * li + 1);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if ((pending & (1u << j)) && (uint32_t)(w0[j] >> 32) == flag_in[j] && (uint32_t)(w1[j] >> 32) == flag_in[j]) {
+            v0[j] = w0[j];
+            v1[j] = w1[j];
+            pending &= ~(1u << j);
+          }
+        }
+      }
+      if (verdict) {
+        stop = true;
+        if (verdict != kStopQuiet) raise_error(wc, verdict);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < nin) {
+        const u32x2 y = u32x2{(uint32_t)v0[j], (uint32_t)v1[j]};
         x = (lp || j > 0) ? VOp<DT, OP>::v2(x, y) : y;
       }
     }
