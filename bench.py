@@ -237,6 +237,9 @@ def size_sweep(args) -> int:
     comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo)
     size = 8
     k = 0
+    while size < args.sweep_min_bytes:
+        size *= 2
+        k += 1
     while size <= args.sweep_max_bytes:
         count = size // 4
         send = synth.device_inputs(4, n, count, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
@@ -292,6 +295,7 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="message-size sweep instead (16 ranks, int32, 8 B .. 256 MiB per rank, 16 channels, "
                          "auto protocol): one JSON line per size")
+    ap.add_argument("--sweep-min-bytes", type=int, default=8)
     ap.add_argument("--sweep-max-bytes", type=int, default=256 << 20)
     ap.add_argument("--sweep-ranks", type=int, default=16)
     ap.add_argument("--sweep-channels", type=int, default=16)
