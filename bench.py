@@ -234,7 +234,8 @@ def size_sweep(args) -> int:
     import synth
 
     n, nch = args.sweep_ranks, args.sweep_channels
-    comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo)
+    comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo,
+                        line_workgroups_per_channel=args.line_wpc or None)
     size = 8
     k = 0
     while size < args.sweep_min_bytes:
@@ -269,7 +270,7 @@ def size_sweep(args) -> int:
         busbw = size / t * bus_factor("allreduce", n) / 1e9
         byts = algorithmic_bytes("allreduce", n, size)
         print(json.dumps({"nranks": n, "nchannels": nch, "bytes_per_rank": size, "algo": algo, "proto": proto,
-                          "us": round(t * 1e6, 2),
+                          "wpc": info["last_workgroups_per_channel"], "us": round(t * 1e6, 2),
                           "busbw_gbs": round(busbw, 3), "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
                           "sampled_parity": ok}), flush=True)
         if not ok:
@@ -290,6 +291,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--wpc", type=int, default=0, help="workgroups per channel (0 = library default)")
+    ap.add_argument("--line-wpc", type=int, default=0,
+                    help="most workgroups per channel of a FLAG/WIDE launch: 1, 2, 4, 8 (0 = per call)")
     ap.add_argument("--slot-bytes", type=int, default=0)
     ap.add_argument("--nslots", type=int, default=0)
     ap.add_argument("--sweep", action="store_true",

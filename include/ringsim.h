@@ -144,6 +144,10 @@ typedef struct {
   int timeout_ms;              /* bound on any single wait; default 10000, env RINGSIM_TIMEOUT_MS */
   size_t flag_threshold_bytes; /* AUTO: FLAG below this many bytes per rank; default 0 = cost model */
   int algo;                    /* ringsim_algo_t for all-reduces; default AUTO, env RINGSIM_ALGO=ring|tree|auto */
+  int line_workgroups_per_channel; /* FLAG/WIDE: most workgroups per (rank, channel) of a launch: 1, 2, 4
+                                      or 8 (fewer where the device cannot hold them all); default 0 = per
+                                      call, the fewest that make every step of a workgroup at most 128
+                                      lines; env RINGSIM_LINE_WPC */
 } ringsim_config_t;
 
 /* Read-only description of a communicator. */
@@ -158,7 +162,8 @@ typedef struct {
   size_t slot_bytes;
   size_t flag_threshold_bytes;
   size_t fifo_bytes;           /* bulk FIFO bytes in HBM */
-  size_t flag_fifo_bytes;      /* flag-packed FIFO bytes in HBM (FLAG and WIDE share it) */
+  size_t flag_fifo_bytes;      /* flag-packed FIFO bytes in HBM (FLAG and WIDE share it; one array per
+                                  line workgroup count 1, 2, 4, 8 up to the largest this device takes) */
   int max_resident_workgroups; /* co-resident workgroups the device can hold */
   int compute_units;
   uint64_t calls;              /* collective calls enqueued so far */
@@ -167,12 +172,14 @@ typedef struct {
   int tree_channels;           /* most channels per tree an all-reduce may use */
   size_t tree_fifo_bytes;      /* double-tree FIFO bytes in HBM */
   int last_algo;               /* algorithm of the latest all-reduce: RINGSIM_ALGO_RING/TREE, 0 if none */
+  int line_max_workgroups_per_channel; /* most workgroups per channel a FLAG/WIDE launch may take */
+  int last_workgroups_per_channel;     /* workgroups per channel of the latest ring call, 0 if none */
 } ringsim_comm_info_t;
 
 /* Fills *cfg with the defaults. Environment overrides, read by this call:
  * RINGSIM_CHUNK_BYTES, RINGSIM_WPC, RINGSIM_SLOT_BYTES, RINGSIM_NSLOTS,
- * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD, RINGSIM_ALGO; RINGSIM_DEBUG=WARN|INFO logs to
- * stderr. Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
+ * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD, RINGSIM_ALGO, RINGSIM_LINE_WPC;
+ * RINGSIM_DEBUG=WARN|INFO logs to stderr. Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
  * the workgroups of simulated rank r return at once, so that the bounded
  * waits of its neighbours expire and the failure path can be exercised. */
 ringsim_result_t ringsim_config_default(ringsim_config_t* cfg);

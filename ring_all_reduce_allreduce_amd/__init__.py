@@ -70,6 +70,7 @@ class Config(ctypes.Structure):
         ("timeout_ms", ctypes.c_int),
         ("flag_threshold_bytes", ctypes.c_size_t),
         ("algo", ctypes.c_int),
+        ("line_workgroups_per_channel", ctypes.c_int),
     ]
 
 
@@ -94,6 +95,8 @@ class CommInfo(ctypes.Structure):
         ("tree_channels", ctypes.c_int),
         ("tree_fifo_bytes", ctypes.c_size_t),
         ("last_algo", ctypes.c_int),
+        ("line_max_workgroups_per_channel", ctypes.c_int),
+        ("last_workgroups_per_channel", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:
@@ -180,7 +183,7 @@ def comm_init(nranks: int, nchannels: int, proto: str | int = "auto", **config) 
     """Creates a communicator. Keyword tunables: chunk_bytes,
     workgroups_per_channel, slot_bytes, nslots, timeout_ms,
     flag_threshold_bytes, algo ("auto", "ring", "tree"; 0 or absent = library
-    default)."""
+    default), line_workgroups_per_channel (1, 2, 4 or 8; 0 = per call)."""
     p = PROTOS[proto] if isinstance(proto, str) else int(proto)
     if isinstance(config.get("algo"), str):
         config["algo"] = ALGOS[config["algo"]]

@@ -18,7 +18,14 @@
 // Lines carry a flag equal to the low 32 bits of (step + 1), taken from the
 // same monotonic step counters as the bulk protocol, so a line left over from
 // an earlier step (of either format) never matches: that would take 2^32
-// steps on one FIFO. Both formats share one FIFO array.
+// steps on one FIFO. Both formats share one FIFO array per workgroup count.
+//
+// Workgroups per channel: a launch may split every unit over wpc = 1, 2, 4 or
+// 8 workgroups per (rank, channel), each a pipeline of its own (own part of
+// every unit, own counters, own 16 slots). Each wpc has its own FIFO array,
+// so every FIFO byte is only ever written with flags of one pipeline's
+// counters, which only grow: the no-match argument above holds whatever wpc
+// earlier calls used.
 //
 // Steps are walked group by group (StepIter groups): a stage moves at most
 // kLineGroupSteps slots before the next stage runs, which keeps one stage of
@@ -42,6 +49,15 @@ constexpr int kPolWideLd = 16;
 typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Waits until every load and store of the wave has completed (s_waitcnt
+// vmcnt(0); expcnt and lgkmcnt left at their maxima). A step issues it once,
+// where its operands are all in anyway, right before its stores: the
+// compiler cannot tell on which paths the stored values are still in flight
+// from their loads and otherwise waits for every earlier access before each
+// store, so that each store also waits for the ones just issued, one memory
+// round trip per line.
+__device__ __forceinline__ void drain_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int LP, int DT>
 struct LineFmt {
@@ -202,7 +218,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   uint32_t out_slot = (uint32_t)(out_base % (uint64_t)nslots);
 
   const int64_t slice = (int64_t)(a.slot_bytes / 16) * F::PB / E;  // payload elements per slot
-  StepIter<DT, MODE, true> it;  // the line protocols run one workgroup per channel
+  StepIter<DT, MODE> it;
   it.init(a, p.r, p.c, p.w, slice, (int64_t)a.group * slice);
   for (; !it.done; it.next()) {
     const bool recv = it.recv, send = it.send;
@@ -258,6 +274,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
           x = Slot<LP>::payload(v);
           if (lp) x = reduce_payload<DT, OP, F::PD>(x, loc);
         }
+        drain_loads();
         if (send) fout.store(li, x, flag_out);
         if (up) store_user<DT, F::PD>(up + (int64_t)li * F::PB, ur, li * F::PB, x, valid, a.vec_ok);
       }
@@ -321,6 +338,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) x[u] = loc[u];
       }
+      drain_loads();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int li = threadIdx.x + u * kThreads;

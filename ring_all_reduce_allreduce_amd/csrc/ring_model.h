@@ -4,20 +4,34 @@
 // collective's latency is nSteps hops of a per-hop latency, its bandwidth term
 // is the bytes it moves over the achievable bandwidth (bus bandwidth times
 // nRanks / nSteps), and the flag-packed protocols pay for their flags: LL
-// half the bandwidth, LL128 a sixteenth. Here the two terms overlap (the
-// ring pipelines steps while the first chunks are still in flight), so they
-// are combined as a 2-norm rather than added:
+// half the bandwidth, LL128 a sixteenth.
 //
-//   t(proto) = base + sqrt((hops * hop_latency)^2 + (bytes / bandwidth)^2)
+// Bulk protocol: the latency and bandwidth terms overlap (the ring pipelines
+// steps while the first chunks are still in flight), so they are combined as
+// a 2-norm rather than added:
+//
+//   t = base + sqrt((hops * hop_latency)^2 + (bytes / bandwidth)^2)
 //
 // with hops = 2(N-1) for the all-reduce and N-1 for reduce-scatter and
-// all-gather, bytes = the HBM bytes of the method (FIFO bytes scaled by the
-// line format: x2 for the flag protocol's 8-of-16-byte lines, x4/3 for the
-// wide protocol's 12-of-16), and constants fitted to bench.py --sweep on
-// MI355X (16 and 8 ranks and channels, 8 B .. 64 MiB per rank): a hop costs
-// ~1.0 us (flag), ~1.1 us (wide) or ~2.45 us (bulk) when every chunk of
-// the ring is busy; one line-protocol workgroup sustains ~11.5 (flag) or
-// ~14 (wide) GB/s of method bytes, the bulk kernel ~6.9 TB/s in total.
+// all-gather and bytes = the HBM bytes of the method; a hop costs ~2.45 us
+// and the kernel sustains ~6.9 TB/s.
+//
+// Line protocols (FLAG, WIDE): a workgroup moves its part of every stage in
+// steps of at most one slot, and its speed is set by steps, not bytes. The
+// first step of every stage waits for the neighbour's previous stage (a hop);
+// further steps of the same stage find their lines already written and cost
+// a step time. Both grow with the lines of a step (lines per thread), and
+// both grow when more workgroups than compute units share the device:
+//
+//   t = base + crowd * (hops * hop(L) + stages * (steps - 1) * step(L))
+//
+// with L the lines of a workgroup's step, steps the slot steps of one stage
+// of one workgroup (all loops), hop(L) = a + b * L / 256, step(L) likewise,
+// crowd = 1 + c * (workgroups / CUs - 1) above one workgroup per CU. The
+// constants are fitted to bench.py sweeps on MI355X (4, 8 and 16 ranks with
+// as many channels, 1, 2, 4 and 8 workgroups per channel, 4 KiB .. 8 MiB per
+// rank); the library evaluates every workgroup count it may launch and takes
+// the fastest.
 #pragma once
 
 #include <algorithm>
@@ -30,10 +44,14 @@ enum ModelProto : int { kModelBulk = 0, kModelFlag = 1, kModelWide = 2 };
 
 struct RingModel {
   double base_us = 3.0;
-  double hop_us[3] = {2.45, 1.0, 1.1};  // bulk, flag, wide
-  double wg_gbs[3] = {0.0, 11.5, 14.0};   // line protocols: per (rank, channel) workgroup
-  double line_max_gbs = 4000.0;           // line protocols' ceiling
+  double bulk_hop_us = 2.45;
   double bulk_gbs = 6900.0;
+  // Line protocols, [FLAG, WIDE][a, b]: per hop and per further step,
+  // a + b * lines / 256 microseconds.
+  double line_base_us = 6.45;
+  double line_hop_us[2][2] = {{0.700, 0.631}, {0.795, 0.341}};
+  double line_step_us[2][2] = {{1.005, 0.103}, {0.953, 0.097}};
+  double line_crowd = 0.515;
   // Double-binary tree (flag lines): per-hop latency, per-workgroup rate of
   // the ring-equivalent flag bytes, and the tree's ceiling.
   double tree_hop_us = 1.25;
@@ -55,13 +73,44 @@ inline double model_bytes(int coll, int nranks, double s, int proto) {
   return user + fifo_factor(proto) * fifo;
 }
 
-// Predicted microseconds of one call.
-inline double model_us(const RingModel& m, int coll, int nranks, int nchannels, double bytes_per_rank, int proto) {
+inline double model_hops(int coll, int nranks) {
+  return coll == kModelAllReduce ? 2.0 * (nranks - 1) : (double)(nranks - 1);
+}
+
+// Predicted microseconds of a bulk-protocol call.
+inline double bulk_model_us(const RingModel& m, int coll, int nranks, double bytes_per_rank) {
   if (nranks <= 1) return m.base_us;
-  const double hops = coll == kModelAllReduce ? 2.0 * (nranks - 1) : (double)(nranks - 1);
-  const double bytes = model_bytes(coll, nranks, bytes_per_rank, proto);
-  const double gbs = proto == kModelBulk ? m.bulk_gbs : std::min(m.line_max_gbs, m.wg_gbs[proto] * nranks * nchannels);
-  return m.base_us + std::hypot(hops * m.hop_us[proto], bytes / (gbs * 1e3));
+  const double bytes = model_bytes(coll, nranks, bytes_per_rank, kModelBulk);
+  return m.base_us + std::hypot(model_hops(coll, nranks) * m.bulk_hop_us, bytes / (m.bulk_gbs * 1e3));
+}
+
+// Shape of a line launch: workgroups per channel, payload bytes per line,
+// lines per slot, chunk bytes, and the device's compute units.
+struct LineShape {
+  int wpc;
+  double payload;
+  double slot_lines;
+  double chunk_bytes;
+  int cus;
+};
+
+// Predicted microseconds of a line-protocol (FLAG or WIDE) call. Every
+// collective moves S / (N * C) bytes per stage of one (rank, channel), in
+// units of at most one chunk.
+inline double line_model_us(const RingModel& m, int coll, int nranks, int nchannels, double bytes_per_rank, int proto,
+                            const LineShape& sh) {
+  if (nranks <= 1) return m.base_us;
+  const int k = proto == kModelWide ? 1 : 0;
+  const double stage_bytes = bytes_per_rank / ((double)nranks * nchannels);
+  const double unit = std::min(stage_bytes, sh.chunk_bytes);
+  const double lines = std::min(std::ceil(unit / sh.wpc / sh.payload), sh.slot_lines);
+  const double steps = std::max(1.0, std::ceil(std::ceil(stage_bytes / sh.wpc / sh.payload) / sh.slot_lines));
+  const double hops = model_hops(coll, nranks);
+  const double wgs = (double)nranks * nchannels * sh.wpc;
+  const double crowd = 1.0 + m.line_crowd * std::max(0.0, wgs / sh.cus - 1.0);
+  const double hop = m.line_hop_us[k][0] + m.line_hop_us[k][1] * lines / 256.0;
+  const double step = m.line_step_us[k][0] + m.line_step_us[k][1] * lines / 256.0;
+  return m.line_base_us + crowd * (hops * hop + (hops + 1.0) * (steps - 1.0) * step);
 }
 
 // Predicted microseconds of a double-binary-tree all-reduce: the reduce

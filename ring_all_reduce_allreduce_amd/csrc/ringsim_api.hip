@@ -80,6 +80,10 @@ struct ringsim_comm {
   int nchannels;
   int proto;
   int wpc;
+  int pipe_mul;     // counter pipelines per channel: max(wpc, line_wpc_max)
+  int line_wpc_max; // most workgroups per channel a line launch may take (power of two)
+  int line_wpc_cfg; // configured line workgroups per channel, 0 = per call
+  int line_per_cu[3];  // resident line workgroups per CU: multi, one, half kernels
   int nslots;
   int device;
   size_t chunk_bytes;
@@ -102,6 +106,7 @@ struct ringsim_comm {
   uint32_t* host_words_dev;  // the same words as the device sees them
   uint64_t calls;
   int last_proto;
+  int last_wpc;
   int algo;                // configured all-reduce algorithm
   int last_algo;
   int tree_channels;       // channels per tree in the tree FIFO arrays
@@ -181,8 +186,8 @@ void fill_common(const ringsim_comm* c, RingArgs* a, const void* const* sb, void
   a->nranks = c->nranks;
   a->nchannels = c->nchannels;
   a->ctr = c->ctr;
-  a->pipe_stride = c->nchannels * c->wpc;
-  a->pipe_mul = c->wpc;
+  a->pipe_stride = c->nchannels * c->pipe_mul;
+  a->pipe_mul = c->pipe_mul;
   a->dev_abort = c->dev_abort;
   a->host_abort = c->host_words_dev;
   a->host_err = c->host_words_dev + 1;
@@ -190,42 +195,26 @@ void fill_common(const ringsim_comm* c, RingArgs* a, const void* const* sb, void
   a->skip_rank = c->skip_rank;
 }
 
-// The protocol of one call. A fixed protocol is taken as configured; AUTO
-// takes the flag protocol below a configured threshold and bulk above it,
-// else the protocol the cost model predicts fastest. Every protocol walks the
-// same partition (the line protocols walk each loop in groups of
-// kLineGroupSteps slots), so the choice never changes a result bit.
-int pick_proto(const ringsim_comm* c, int mode, size_t bytes_per_rank) {
-  if (c->proto != RINGSIM_PROTO_AUTO) return c->proto;
-  if (c->flag_threshold) return bytes_per_rank < c->flag_threshold ? RINGSIM_PROTO_FLAG : RINGSIM_PROTO_BULK;
-  const RingModel m;
-  int best = RINGSIM_PROTO_BULK;
-  double best_us = model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, kModelBulk);
-  const int line_protos[2][2] = {{RINGSIM_PROTO_FLAG, kModelFlag}, {RINGSIM_PROTO_WIDE, kModelWide}};
-  for (const auto& lp : line_protos) {
-    const double us = model_us(m, mode, c->nranks, c->nchannels, (double)bytes_per_rank, lp[1]);
-    if (us < best_us) {
-      best_us = us;
-      best = lp[0];
-    }
-  }
-  return best;
-}
-
 int model_proto(int proto) {
   return proto == RINGSIM_PROTO_FLAG ? kModelFlag : proto == RINGSIM_PROTO_WIDE ? kModelWide : kModelBulk;
 }
 
-// Fills the protocol-dependent launch geometry.
-void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize) {
+// Fills the protocol-dependent launch geometry; line_wpc is the workgroup
+// count of a line launch (1, 2, 4 or 8). The flag FIFO holds one array per
+// count, in increasing order, each [rank][channel][part][slot] with
+// kFlagSlots slots of line_slot_bytes(count) per part.
+void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int line_wpc = 1) {
   a->chunk = (int64_t)c->chunk_bytes / esize;
   if (proto == RINGSIM_PROTO_FLAG || proto == RINGSIM_PROTO_WIDE) {
-    a->wpc = 1;  // the line kernels walk whole chunks: one workgroup per (rank, channel)
-    a->fifo = c->flag_fifo;
-    a->fifo_stride = c->nchannels;
-    a->fifo_mul = 1;
+    const size_t nc = (size_t)c->nranks * c->nchannels;
+    size_t off = 0;
+    for (int w = 1; w < line_wpc; w *= 2) off += nc * (size_t)line_level_bytes(w);
+    a->wpc = line_wpc;
+    a->fifo = c->flag_fifo + off;
+    a->fifo_stride = c->nchannels * line_wpc;
+    a->fifo_mul = line_wpc;
     a->nslots = kFlagSlots;
-    a->slot_bytes = kFlagSlotBytes;
+    a->slot_bytes = line_slot_bytes(line_wpc);
     a->group = kLineGroupSteps;
   } else {
     a->wpc = c->wpc;
@@ -247,6 +236,110 @@ int64_t max_unit_bytes(const RingArgs& a, int mode, int esize) {
   const int64_t l0 = channel_span(a.count, a.nchannels, A);
   const int64_t cur = mode == kAllReduce ? ar_loop_chunk(l0, a.nranks, a.chunk, A) : min64(a.chunk, l0);
   return align_up(div_up(cur, a.wpc), A) * esize;
+}
+
+// Line kernels by lines per step (host mirror of the device LineMode).
+enum HostLineMode : int { kHostLinesMulti = 0, kHostLinesOne = 1, kHostLinesHalf = 2 };
+
+struct LinePlan {
+  int wpc;
+  int mode;       // HostLineMode
+  int64_t steps;  // slot steps of the longest unit part
+};
+
+// The line kernel a launch with `wpc` workgroups per channel needs: the
+// longest step is the longest unit part or a whole slot, whichever is
+// shorter.
+LinePlan line_plan(const RingArgs& a, int mode, int esize, int line_proto, int dtype, int wpc) {
+  const int64_t payload = line_proto == kLineWide && dtype != RINGSIM_INT64 ? 12 : 8;
+  RingArgs t = a;
+  t.wpc = wpc;
+  const int64_t unit_lines = div_up(max_unit_bytes(t, mode, esize), payload);
+  const int64_t slot_lines = line_slot_bytes(wpc) / 16;
+  const int64_t lines = std::min(unit_lines, slot_lines);
+  const int m = lines <= kThreads / 2 ? kHostLinesHalf : lines <= kThreads ? kHostLinesOne : kHostLinesMulti;
+  return LinePlan{wpc, m, div_up(unit_lines, slot_lines)};
+}
+
+bool line_plan_resident(const ringsim_comm* c, const LinePlan& lp) {
+  return (int64_t)c->nranks * c->nchannels * lp.wpc <= (int64_t)c->line_per_cu[lp.mode] * c->compute_units;
+}
+
+// Shape of a call of `count` elements, as the planners see it.
+RingArgs call_shape(const ringsim_comm* c, size_t count, int esize) {
+  RingArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.count = (int64_t)count;
+  a.nranks = c->nranks;
+  a.nchannels = c->nchannels;
+  a.chunk = (int64_t)c->chunk_bytes / esize;
+  a.wpc = 1;
+  return a;
+}
+
+struct ProtoChoice {
+  int proto;
+  LinePlan plan;  // line protocols: workgroups per channel and kernel
+  double us;      // predicted time
+};
+
+// A line protocol's launch: the configured workgroup count (the most that
+// the device can hold at once, if fewer), else among 1, 2, 4, 8 (up to the
+// comm's maximum) whose kernel can be resident at once, with at most two
+// workgroups per compute unit, the count the cost model predicts fastest.
+// One workgroup per channel is always resident (comm init checks it).
+ProtoChoice pick_line(const ringsim_comm* c, const RingArgs& a, int mode, int dtype, int proto, double bytes) {
+  const int esize = dtype_size(dtype);
+  const int lp = proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag;
+  const RingModel m;
+  const int64_t nc = (int64_t)c->nranks * c->nchannels;
+  const int top = c->line_wpc_cfg ? std::min(c->line_wpc_cfg, c->line_wpc_max) : c->line_wpc_max;
+  ProtoChoice best;
+  best.proto = proto;
+  best.us = -1.0;
+  for (int w = 1; w <= top; w *= 2) {
+    const LinePlan plan = line_plan(a, mode, esize, lp, dtype, w);
+    if (w > 1 && (!line_plan_resident(c, plan) || (!c->line_wpc_cfg && nc * w > 2 * (int64_t)c->compute_units)))
+      continue;
+    const LineShape sh{w, lp == kLineWide && dtype != RINGSIM_INT64 ? 12.0 : 8.0,
+                       (double)(line_slot_bytes(w) / 16), (double)c->chunk_bytes, c->compute_units};
+    const double us = line_model_us(m, mode, c->nranks, c->nchannels, bytes, model_proto(proto), sh);
+    // A configured count is taken as the most that may run, not a hint.
+    if (best.us < 0.0 || (c->line_wpc_cfg ? w > best.plan.wpc : us < best.us)) {
+      best.plan = plan;
+      best.us = us;
+    }
+  }
+  return best;
+}
+
+// The protocol of one call. A fixed protocol is taken as configured; AUTO
+// takes the flag protocol below a configured threshold and bulk above it,
+// else the protocol the cost model predicts fastest, each line protocol with
+// the workgroups its launch would take. Every protocol walks the same
+// partition (the line protocols walk each loop in groups of kLineGroupSteps
+// slots), so the choice never changes a result bit.
+ProtoChoice pick_proto(const ringsim_comm* c, int mode, size_t count, int dtype) {
+  const int esize = dtype_size(dtype);
+  const RingArgs a = call_shape(c, count, esize);
+  const double bytes = (double)((mode == kAllReduce ? count : count * c->nranks) * esize);
+  auto bulk = [&]() {
+    ProtoChoice pc;
+    pc.proto = RINGSIM_PROTO_BULK;
+    pc.plan = LinePlan{c->wpc, kHostLinesMulti, 0};
+    pc.us = bulk_model_us(RingModel(), mode, c->nranks, bytes);
+    return pc;
+  };
+  if (c->proto == RINGSIM_PROTO_FLAG || c->proto == RINGSIM_PROTO_WIDE) return pick_line(c, a, mode, dtype, c->proto, bytes);
+  if (c->proto == RINGSIM_PROTO_BULK) return bulk();
+  if (c->flag_threshold)
+    return bytes < (double)c->flag_threshold ? pick_line(c, a, mode, dtype, RINGSIM_PROTO_FLAG, bytes) : bulk();
+  ProtoChoice best = bulk();
+  for (const int p : {RINGSIM_PROTO_FLAG, RINGSIM_PROTO_WIDE}) {
+    const ProtoChoice pc = pick_line(c, a, mode, dtype, p, bytes);
+    if (pc.us < best.us) best = pc;
+  }
+  return best;
 }
 
 ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void* const* rb, size_t bytes,
@@ -273,24 +366,19 @@ int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, c->tree_channels));
 }
 
-// Predicted time of the ring as AUTO would run it.
-double ring_auto_us(const ringsim_comm* c, size_t bytes_per_rank) {
-  const RingModel m;
-  const int proto = pick_proto(c, kAllReduce, bytes_per_rank);
-  return model_us(m, kAllReduce, c->nranks, c->nchannels, (double)bytes_per_rank, model_proto(proto));
-}
 
 // AUTO's algorithm: the tree only where the fold order cannot show in the
 // result (integers wrap associatively; max/min pick one input), only when
 // the flag-packed lines it moves are allowed (protocol AUTO or FLAG), and
 // only when it is predicted to be faster than the ring.
-bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t bytes_per_rank) {
+bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t count) {
   const bool order_free = dtype == RINGSIM_INT32 || dtype == RINGSIM_INT64 || op == RINGSIM_MAX || op == RINGSIM_MIN;
   const bool lines_ok = c->proto == RINGSIM_PROTO_AUTO || c->proto == RINGSIM_PROTO_FLAG;
   if (!order_free || !lines_ok || c->tree_channels < 1) return false;
   const RingModel m;
+  const size_t bytes_per_rank = count * (size_t)dtype_size(dtype);
   return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank), (double)bytes_per_rank) <
-         ring_auto_us(c, bytes_per_rank);
+         pick_proto(c, kAllReduce, count, dtype).us;
 }
 
 ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const* rb, size_t count, int dtype,
@@ -350,32 +438,32 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
     // A single rank is a local copy ("NCCL" book, enqueue chapter, taskAppend).
     return launch_local_copy(c, sb, rb, count * esize, s);
   }
-  const size_t per_rank_bytes = (mode == kAllReduce ? count : count * n) * esize;
   if (mode == kAllReduce) {
     const bool tree = c->algo == RINGSIM_ALGO_TREE ||
-                      (c->algo == RINGSIM_ALGO_AUTO && auto_picks_tree(c, dtype, op, per_rank_bytes));
+                      (c->algo == RINGSIM_ALGO_AUTO && auto_picks_tree(c, dtype, op, count));
     c->last_algo = tree ? RINGSIM_ALGO_TREE : RINGSIM_ALGO_RING;
     if (tree) return launch_tree(c, sb, rb, count, dtype, op, vec, s);
   }
   RingArgs a;
   fill_common(c, &a, sb, rb);
   a.count = (int64_t)count;
-  const int proto = pick_proto(c, mode, per_rank_bytes);
-  fill_proto(c, &a, proto, esize);
+  const ProtoChoice pc = pick_proto(c, mode, count, dtype);
+  const int proto = pc.proto;
+  fill_proto(c, &a, proto, esize, pc.plan.wpc);
   // Vector moves need every unit to start on a 16-byte boundary; for the
   // block-strided collectives that requires whole 16-byte blocks.
   a.vec_ok = vec && (mode == kAllReduce || (count * esize) % 16 == 0);
   c->last_proto = proto;
   hipError_t e;
   if (proto == RINGSIM_PROTO_BULK) {
+    c->last_wpc = a.wpc;
     e = launch_ring_bulk(a, mode, dtype, op, s);
   } else {
     const int lp = proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag;
-    const int64_t line_payload = lp == kLineWide && dtype != RINGSIM_INT64 ? 12 : 8;
-    const int64_t unit = max_unit_bytes(a, mode, esize);
-    e = unit <= (int64_t)(kThreads / 2) * line_payload ? launch_ring_lines_half(a, lp, mode, dtype, op, s)
-        : unit <= (int64_t)kThreads * line_payload     ? launch_ring_lines_one(a, lp, mode, dtype, op, s)
-                                                       : launch_ring_lines_multi(a, lp, mode, dtype, op, s);
+    c->last_wpc = a.wpc;
+    e = pc.plan.mode == kHostLinesHalf  ? launch_ring_lines_half(a, lp, mode, dtype, op, s)
+        : pc.plan.mode == kHostLinesOne ? launch_ring_lines_one(a, lp, mode, dtype, op, s)
+                                        : launch_ring_lines_multi(a, lp, mode, dtype, op, s);
   }
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "kernel launch failed: %s", hipGetErrorString(e));
@@ -414,6 +502,7 @@ ringsim_result_t ringsim_config_default(ringsim_config_t* cfg) {
   cfg->timeout_ms = (int)env_long("RINGSIM_TIMEOUT_MS", 10000);
   cfg->flag_threshold_bytes = (size_t)env_long("RINGSIM_FLAG_THRESHOLD", 0);
   cfg->algo = env_algo(RINGSIM_ALGO_AUTO);
+  cfg->line_workgroups_per_channel = (int)env_long("RINGSIM_LINE_WPC", 0);
   return RINGSIM_SUCCESS;
 }
 
@@ -437,6 +526,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
     if (user_cfg->timeout_ms) cfg.timeout_ms = user_cfg->timeout_ms;
     if (user_cfg->flag_threshold_bytes) cfg.flag_threshold_bytes = user_cfg->flag_threshold_bytes;
     if (user_cfg->algo) cfg.algo = user_cfg->algo;
+    if (user_cfg->line_workgroups_per_channel) cfg.line_workgroups_per_channel = user_cfg->line_workgroups_per_channel;
   }
   if (cfg.algo < RINGSIM_ALGO_AUTO || cfg.algo > RINGSIM_ALGO_TREE) return RINGSIM_INVALID_ARGUMENT;
   if (cfg.chunk_bytes == 0 || cfg.chunk_bytes % 16 || cfg.chunk_bytes > ((size_t)1 << 30))
@@ -447,6 +537,10 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   if (cfg.workgroups_per_channel < 0 || cfg.workgroups_per_channel > RINGSIM_MAX_WORKGROUPS_PER_CHANNEL)
     return RINGSIM_INVALID_ARGUMENT;
   if (cfg.timeout_ms <= 0) return RINGSIM_INVALID_ARGUMENT;
+  {
+    const int lw = cfg.line_workgroups_per_channel;
+    if (lw < 0 || lw > kMaxLineWpc || (lw & (lw - 1))) return RINGSIM_INVALID_ARGUMENT;
+  }
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
@@ -458,8 +552,9 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Bulk steps stage their own operand in LDS (double-buffered) unless the
   // slot is too large or RINGSIM_LDS_STAGE=0.
   const int lds_stage = cfg.slot_bytes <= (size_t)kMaxStagedSlotBytes && env_long("RINGSIM_LDS_STAGE", 1) != 0;
-  const int per_cu = std::min({bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_half_blocks_per_cu(),
-                               line_one_blocks_per_cu(), line_multi_blocks_per_cu()});
+  const int line_per_cu[3] = {line_multi_blocks_per_cu(), line_one_blocks_per_cu(), line_half_blocks_per_cu()};
+  const int per_cu = std::min({bulk_blocks_per_cu(lds_stage ? 2 * cfg.slot_bytes : 0), line_per_cu[0],
+                               line_per_cu[1], line_per_cu[2]});
   if (per_cu <= 0) return RINGSIM_UNHANDLED_DEVICE_ERROR;
   const int64_t max_resident = (int64_t)per_cu * cus;
 
@@ -473,6 +568,15 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
                                                                     (2 * (int64_t)cus) / nc));
   while (wpc > 1 && nc * wpc > max_resident) --wpc;
   if (nc * wpc > max_resident) return RINGSIM_INVALID_USAGE;
+
+  // Line launches: up to kMaxLineWpc workgroups per channel, as many as the
+  // device can hold with the line kernel that holds the most (the kernel a
+  // launch needs is checked per call).
+  const int line_best_cu = std::max({line_per_cu[0], line_per_cu[1], line_per_cu[2]});
+  int line_wpc_max = 1;
+  while (line_wpc_max < kMaxLineWpc && nc * line_wpc_max * 2 <= (int64_t)line_best_cu * cus) line_wpc_max *= 2;
+  size_t line_fifo_per_nc = 0;
+  for (int w = 1; w <= line_wpc_max; w *= 2) line_fifo_per_nc += (size_t)line_level_bytes(w);
 
   // FIFO depth: one stage of one workgroup may fill at most half of its FIFO,
   // as NCCL's chunkSteps = NCCL_STEPS/2 ("NCCL" book, enqueue chapter,
@@ -496,6 +600,10 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->nchannels = nchannels;
   c->proto = proto;
   c->wpc = wpc;
+  c->line_wpc_max = line_wpc_max;
+  c->line_wpc_cfg = cfg.line_workgroups_per_channel;
+  c->pipe_mul = std::max(wpc, line_wpc_max);
+  for (int k = 0; k < 3; ++k) c->line_per_cu[k] = line_per_cu[k];
   c->nslots = nslots;
   c->device = dev;
   c->chunk_bytes = cfg.chunk_bytes;
@@ -522,10 +630,9 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
     }
   }
 
-  const int64_t pipes = nc * wpc;
-  c->fifo_bytes = (size_t)pipes * nslots * cfg.slot_bytes;
-  c->flag_fifo_bytes = (size_t)nc * kFlagSlots * kFlagSlotBytes;
-  c->ctr_bytes = (size_t)pipes * sizeof(FifoCtr);
+  c->fifo_bytes = (size_t)(nc * wpc) * nslots * cfg.slot_bytes;
+  c->flag_fifo_bytes = (size_t)nc * line_fifo_per_nc;
+  c->ctr_bytes = (size_t)(nc * c->pipe_mul) * sizeof(FifoCtr);
   const size_t tree_fifos = (size_t)2 * tree_channels * nranks * 2;
   c->tree_fifo_bytes = tree_fifos * kTreeSlots * kTreeSlotBytes;
   c->tree_ctr_bytes = tree_fifos * sizeof(FifoCtr);
@@ -608,6 +715,8 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
   info->tree_channels = comm->tree_channels;
   info->tree_fifo_bytes = comm->tree_fifo_bytes;
   info->last_algo = comm->last_algo;
+  info->line_max_workgroups_per_channel = comm->line_wpc_max;
+  info->last_workgroups_per_channel = comm->last_wpc;
   return RINGSIM_SUCCESS;
 }
 
@@ -707,9 +816,21 @@ ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t
   if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS)
     return RINGSIM_INVALID_ARGUMENT;
   const RingModel m;
-  *us_bulk = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, kModelBulk);
-  *us_flag = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, kModelFlag);
-  *us_wide = model_us(m, coll, nranks, nchannels, (double)bytes_per_rank, kModelWide);
+  const double b = (double)bytes_per_rank;
+  *us_bulk = bulk_model_us(m, coll, nranks, b);
+  // Line protocols: the fastest of 1, 2, 4, 8 workgroups per channel on a
+  // 256-CU device, at most two workgroups per CU beyond one per channel.
+  for (int k = 0; k < 2; ++k) {
+    const int proto = k ? kModelWide : kModelFlag;
+    double best = -1.0;
+    for (int w = 1; w <= kMaxLineWpc; w *= 2) {
+      if (w > 1 && (int64_t)nranks * nchannels * w > 2 * 256) break;
+      const LineShape sh{w, k ? 12.0 : 8.0, (double)(line_slot_bytes(w) / 16), 524288.0, 256};
+      const double us = line_model_us(m, coll, nranks, nchannels, b, proto, sh);
+      if (best < 0.0 || us < best) best = us;
+    }
+    *(k ? us_wide : us_flag) = best;
+  }
   return RINGSIM_SUCCESS;
 }
 

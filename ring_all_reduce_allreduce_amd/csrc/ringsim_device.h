@@ -290,10 +290,11 @@ __device__ __forceinline__ Pipe locate(const RingArgs& a) {
 // rank r produced, group by group), and a step still reduces the same
 // elements in the same rank order, so values do not change; but a stage puts
 // at most one group into the FIFO, whatever the chunk size.
-// ONE_WG: one workgroup per channel (wpc == 1, the line protocols), so a
-// unit is a whole chunk or block slice and no part split (no division) is
-// needed per unit.
-template <int DT, int MODE, bool ONE_WG = false>
+// Parts: with wpc workgroups per channel, workgroup w moves part w of every
+// unit (alignUp(ceil(n / wpc), A) elements, clamped to the unit). The part
+// bounds of a whole chunk and of the loop's ragged chunk are computed once per
+// loop, so a stage costs no division.
+template <int DT, int MODE>
 struct StepIter {
   static constexpr int64_t E = sizeof(typename Elem<DT>::T);
   static constexpr int64_t A = 16 / E;
@@ -304,10 +305,13 @@ struct StepIter {
   int slice;  // elements per step (a slot's payload)
   int N, r, w, wpc;
   // loop, group and stage
-  int64_t off, rem, cur, sub_full, part_lo, part_n;
+  int64_t off, rem, cur, part_lo, part_n;
   int glen, g_lo, umax;  // group length, start of the current group, longest unit of the loop
-  int kfull;             // all-reduce, one workgroup per channel: chunks of the loop that are whole
-  int64_t tail;          // ... and the length of chunk kfull (the ragged one, possibly 0)
+  // all-reduce: chunks [0, kfull) of the loop are whole, chunk kfull is the
+  // ragged one (possibly empty), later ones are empty; this workgroup's part
+  // of a whole chunk is [full_lo, full_lo + full_n), of the ragged one
+  // [tail_lo, tail_lo + tail_n)
+  int kfull, full_lo, full_n, tail_lo, tail_n;
   int j, idx;
   // current unit and step
   int64_t local_e, out_e;
@@ -328,17 +332,24 @@ struct StepIter {
     rem = L - off;
     if constexpr (MODE == kAllReduce) {
       cur = ar_loop_chunk(rem, N, chunk, A);
-      sub_full = ONE_WG ? cur : align_up(div_up(cur, wpc), A);
-      umax = (int)sub_full;
-      if constexpr (ONE_WG) {
-        // One division per loop instead of 64-bit clamps per unit: chunk k
-        // is whole for k < kfull, `tail` long for k == kfull, empty beyond.
-        kfull = rem >= (int64_t)N * cur ? N : (int)(rem / cur);
-        tail = kfull < N ? rem - (int64_t)kfull * cur : 0;
+      kfull = rem >= (int64_t)N * cur ? N : (int)(rem / cur);
+      const int64_t tail = kfull < N ? rem - (int64_t)kfull * cur : 0;
+      if (wpc == 1) {
+        full_lo = tail_lo = 0;
+        full_n = (int)cur;
+        tail_n = (int)tail;
+      } else {
+        const Range pf = split_part(cur, wpc, w, A);
+        const Range pt = split_part(tail, wpc, w, A);
+        full_lo = (int)pf.lo;
+        full_n = (int)(pf.hi - pf.lo);
+        tail_lo = (int)pt.lo;
+        tail_n = (int)(pt.hi - pt.lo);
       }
+      umax = full_n;
     } else {
       cur = min64(chunk, rem);
-      if constexpr (ONE_WG) {
+      if (wpc == 1) {
         part_lo = 0;
         part_n = cur;
       } else {
@@ -361,17 +372,9 @@ struct StepIter {
 
   __device__ __forceinline__ void set_unit_range() {
     if constexpr (MODE == kAllReduce) {
-      if constexpr (ONE_WG) {
-        m = idx < kfull ? (int)cur : (idx == kfull ? (int)tail : 0);
-        local_e = out_e = ch_lo + off + (int64_t)idx * cur;
-      } else {
-        const int64_t clo = min64((int64_t)idx * cur, rem);
-        const int64_t n = min64(clo + cur, rem) - clo;
-        const int64_t sub = n == cur ? sub_full : align_up(div_up(n, wpc), A);
-        const int64_t plo = min64((int64_t)w * sub, n);
-        m = (int)(min64(plo + sub, n) - plo);
-        local_e = out_e = ch_lo + off + clo + plo;
-      }
+      const bool whole = idx < kfull;
+      m = whole ? full_n : (idx == kfull ? tail_n : 0);
+      local_e = out_e = ch_lo + off + (int64_t)idx * cur + (whole ? full_lo : tail_lo);
       recv = j >= 1;
       use_local = j <= N - 1;
       send = j <= 2 * N - 3;

@@ -88,6 +88,11 @@ def test_invalid_arguments_fail_before_touching_a_device(L):
     cfg = rs.Config()
     cfg.slot_bytes = 1000
     assert L.ringsim_comm_init_config(ctypes.byref(h), 4, 1, 0, ctypes.byref(cfg)) == 4
+    for lw in (-1, 3, 6, 16):  # line workgroups per channel: 0 (per call), 1, 2, 4 or 8
+        cfg = rs.Config()
+        cfg.line_workgroups_per_channel = lw
+        assert L.ringsim_comm_init_config(ctypes.byref(h), 4, 1, 0, ctypes.byref(cfg)) == 4
+        assert h.value == 12345
     n = ctypes.c_size_t()
     assert L.ringsim_debug_plan(0, 10, 4, 1, 24, 2, None, 0, ctypes.byref(n)) == 4
     assert L.ringsim_debug_plan(0, 10, 4, 1, 16, 9, None, 0, ctypes.byref(n)) == 4
@@ -116,13 +121,14 @@ def test_config_defaults(L):
     assert cfg.nslots == 8
     assert cfg.slot_bytes == 32_768
     assert cfg.flag_threshold_bytes == 0  # 0: AUTO uses the cost model
+    assert cfg.line_workgroups_per_channel == 0  # 0: chosen per call
 
 
 def test_cost_model_shape(L):
     """The model behind AUTO: flag-packed wins for tiny messages and bulk for
     large ones, each protocol's time grows with size and with the hop count
-    2(N-1), and the flag protocol's bandwidth term carries twice the FIFO
-    bytes (the pages' LL factor)."""
+    2(N-1), and the wide lines (12 payload bytes per 16 against 8) need fewer
+    steps than the flag lines once the steps, not the hops, dominate."""
     for n, c in ((4, 4), (8, 8), (16, 16)):
         tiny = rs.debug_model("allreduce", n, c, 8)
         big = rs.debug_model("allreduce", n, c, 256 << 20)
@@ -132,7 +138,7 @@ def test_cost_model_shape(L):
         for k in range(3, 29):
             m = rs.debug_model("allreduce", n, c, 1 << k)
             # the wide lines carry 12 payload bytes per 16 against the flag lines' 8:
-            # once bandwidth dominates they win
+            # once the steps dominate they win
             if k >= 24:
                 assert m["wide_us"] < m["flag_us"]
             if prev:
@@ -144,17 +150,18 @@ def test_cost_model_shape(L):
     ar = rs.debug_model("allreduce", 8, 8, 8)
     rsm = rs.debug_model("reduce_scatter", 8, 8, 8)
     assert rsm["bulk_us"] < ar["bulk_us"]
-    # crossover moves to larger messages as ranks and channels grow (measured on MI355X:
-    # ~64 KiB at 4x4, ~300 KiB at 8x8, ~1 MiB at 16x16)
+    # the line protocols' lead over bulk grows with the ring: measured on MI355X
+    # (C = N, best line protocol and workgroup count against bulk) the crossover is
+    # ~1 MiB at 4x4, ~4 MiB at 8x8 and 4-8 MiB at 16x16
     def crossover(n, c):
         for k in range(3, 30):
             m = rs.debug_model("allreduce", n, c, 1 << k)
-            if m["bulk_us"] <= m["flag_us"]:
+            if m["bulk_us"] <= min(m["flag_us"], m["wide_us"]):
                 return 1 << k
         return 1 << 30
     x4, x8, x16 = crossover(4, 4), crossover(8, 8), crossover(16, 16)
-    assert x4 < x8 < x16
-    assert (16 << 10) <= x4 <= (256 << 10) and (128 << 10) <= x8 <= (1 << 20) and (512 << 10) <= x16 <= (4 << 20)
+    assert x4 < x8 <= x16
+    assert (256 << 10) <= x4 <= (2 << 20) and (1 << 20) <= x8 <= (8 << 20) and (2 << 20) <= x16 <= (16 << 20)
 
 
 def test_library_tree_matches_oracle_tree(L):

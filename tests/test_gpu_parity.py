@@ -307,7 +307,8 @@ def test_line_kernel_variant_boundary(proto, dtype):
     lines (2 KiB of FLAG payload, 3 KiB of WIDE payload, 2 KiB for int64
     lines) and the several-lines kernel above. Units of exactly each limit
     and one 16-byte vector more take different kernels; all must be whole and
-    bit-exact, for the all-reduce, reduce-scatter and all-gather."""
+    bit-exact, for the all-reduce, reduce-scatter and all-gather. One
+    workgroup per channel, so that the unit is the step."""
     e = {"float32": 4, "bfloat16": 2, "int64": 8}[dtype]
     line_payload = 12 if proto == "wide" and dtype != "int64" else 8
     n = 4
@@ -315,12 +316,12 @@ def test_line_kernel_variant_boundary(proto, dtype):
         unit = lines * line_payload // e + extra
         count = n * unit  # one tail loop per channel: chunk = unit
         xs = _inputs(n, count, dtype, 1300 + unit)
-        got = _run_allreduce(xs, dtype, "sum", 1, proto)
+        got = _run_allreduce(xs, dtype, "sum", 1, proto, line_workgroups_per_channel=1)
         want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=1)
         _assert_same(got, want, dtype, f"allreduce {proto} unit={unit}")
         # reduce-scatter / all-gather: one unit per loop of each block
         for coll in ("reduce_scatter", "all_gather"):
-            comm = rs.comm_init(n, 1, proto, chunk_bytes=unit * e)
+            comm = rs.comm_init(n, 1, proto, chunk_bytes=unit * e, line_workgroups_per_channel=1)
             try:
                 if coll == "reduce_scatter":
                     src = _inputs(n, n * unit, dtype, 1400 + unit)
@@ -341,3 +342,90 @@ def test_line_kernel_variant_boundary(proto, dtype):
                 _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"{coll} {proto} unit={unit}")
             finally:
                 rs.comm_destroy(comm)
+
+
+def _run_coll(coll, xs, dtype, nch, proto, chunk_bytes, **cfg):
+    n = len(xs)
+    comm = rs.comm_init(n, nch, proto, chunk_bytes=chunk_bytes, **cfg)
+    try:
+        send = [G.to_device(x, dtype) for x in xs]
+        m = xs[0].shape[0]
+        out = {"allreduce": m, "reduce_scatter": m // n, "all_gather": m * n}[coll]
+        recv = [G.empty_like_rank(out, dtype) for _ in range(n)]
+        G.say(f"{coll} N={n} in={m} dtype={dtype} C={nch} proto={proto} chunk={chunk_bytes} cfg={cfg}")
+        if coll == "allreduce":
+            rs.allreduce(comm, send, recv, op="sum")
+        elif coll == "reduce_scatter":
+            rs.reduce_scatter(comm, send, recv, op="sum")
+        else:
+            rs.all_gather(comm, send, recv)
+        G.sync()
+        G.check_comm_ok(comm)
+        return [G.to_host(t, dtype) for t in recv], rs.comm_query(comm)
+    finally:
+        rs.comm_destroy(comm)
+
+
+@pytest.mark.parametrize("proto", ["flag", "wide"])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int64"])
+def test_line_workgroups_per_channel(proto, dtype):
+    """A line launch may split every unit over 1, 2, 4 or 8 workgroups per
+    (rank, channel), each with its own FIFO slots and counters. The split
+    changes which workgroup moves an element, never the chunk it belongs to,
+    so every count gives the oracle's bits: two full loops and a ragged third
+    per channel, units of several step groups, for all three collectives."""
+    n, nch, chunk = 5, 2, 262_144
+    e = {"float32": 4, "bfloat16": 2, "int64": 8}[dtype]
+    per_channel = 2 * n * chunk + 300 * 1024 + 48
+    count = (nch * per_channel) // e - 3
+    xs = _inputs(n, count, dtype, 1600 + e)
+    want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=nch, chunk_bytes=chunk)
+    for lw in (1, 2, 4, 8):
+        got, info = _run_coll("allreduce", xs, dtype, nch, proto, chunk, line_workgroups_per_channel=lw, algo="ring")
+        assert info["last_workgroups_per_channel"] == lw
+        _assert_same(got, want, dtype, f"allreduce {proto} line wpc {lw}")
+    rc = (3 * chunk + 20_000) // e + 1  # three loops per block, the last ragged
+    src = _inputs(n, n * rc, dtype, 1700 + e)
+    want_rs = oracle.ring_reduce_scatter(src, "sum", dtype, nchannels=nch, chunk_bytes=chunk)
+    sc = (chunk + 5000) // e + 3
+    src_ag = _inputs(n, sc, dtype, 1800 + e)
+    want_ag = oracle.ring_all_gather(src_ag, dtype, nchannels=nch, chunk_bytes=chunk)
+    for lw in (2, 8):
+        got, _ = _run_coll("reduce_scatter", src, dtype, nch, proto, chunk, line_workgroups_per_channel=lw)
+        _assert_same(got, want_rs, dtype, f"reduce_scatter {proto} line wpc {lw}")
+        got, _ = _run_coll("all_gather", src_ag, dtype, nch, proto, chunk, line_workgroups_per_channel=lw)
+        _assert_same(got, want_ag, dtype, f"all_gather {proto} line wpc {lw}")
+
+
+@pytest.mark.parametrize("proto", ["flag", "wide"])
+def test_line_workgroup_counts_switch_on_one_comm(proto):
+    """Consecutive calls of one communicator take different workgroup counts
+    per channel (each count has a FIFO array of its own, and a line's flag is
+    a step of the one pipeline that owns that array part, so no line left by
+    an earlier call can match). The cost model splits a stage of 1, 2, 4 and
+    16 lines per (rank, channel) over 1, 2, 4 and 8 workgroups (fewer lines
+    per step is faster, ties go to fewer workgroups). Two rounds through the
+    sizes, then larger messages, fresh data every call, every result
+    checked."""
+    n, nch, dtype = 8, 4, "float32"
+    payload = 12 if proto == "wide" else 8
+    comm = rs.comm_init(n, nch, proto)
+    try:
+        cases = []
+        sizes = [(lines * payload * n * nch) // 4 for lines in (1, 2, 4, 16)] * 2
+        sizes += [(lines * payload * n * nch) // 4 - 5 for lines in (100, 300, 900, 3000)]
+        for k, count in enumerate(sizes):
+            xs = _inputs(n, count, dtype, 1900 + k)
+            send = [G.to_device(x, dtype) for x in xs]
+            recv = [G.empty_like_rank(count, dtype) for _ in range(n)]
+            G.say(f"switch {proto} call {k} count={count}")
+            rs.allreduce(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            cases.append((xs, recv, count, rs.comm_query(comm)["last_workgroups_per_channel"]))
+        assert [c[3] for c in cases[:8]] == [1, 2, 4, 8] * 2
+        for xs, recv, count, lw in cases:
+            want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=nch)
+            _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"switch count={count} wpc={lw}")
+    finally:
+        rs.comm_destroy(comm)
