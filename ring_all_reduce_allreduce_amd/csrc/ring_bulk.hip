@@ -100,8 +100,8 @@ __device__ __forceinline__ void move_slice(int64_t n, const char* fin, const cha
   using T = typename Elem<DT>::T;
   constexpr int A = 16 / (int)sizeof(T);
   const int64_t nv = vec_ok ? n / A : 0;
-  const rsrc_t rin = make_rsrc(fin, fin ? slot_bytes : 0);
-  const rsrc_t rout = make_rsrc(fout, fout ? slot_bytes : 0);
+  const rsrc_t rin = make_uniform_rsrc(fin, fin ? slot_bytes : 0);
+  const rsrc_t rout = make_uniform_rsrc(fout, fout ? slot_bytes : 0);
   const u32x4* l4 = reinterpret_cast<const u32x4*>(loc);
   u32x4* u4 = reinterpret_cast<u32x4*>(uout);
   if (nv > 0 && staged && loc) {
@@ -171,8 +171,8 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
     s_base[1] = ld_relaxed(&p.out_ctr->tail);
   }
   __syncthreads();
-  const uint64_t in_base = s_base[0];
-  const uint64_t out_base = s_base[1];
+  const uint64_t in_base = uniform64(s_base[0]);
+  const uint64_t out_base = uniform64(s_base[1]);
   const uint64_t nslots = (uint64_t)a.nslots;
   const int64_t stage_vecs = a.slot_bytes / 16;
   uint64_t nrecv = 0, nsent = 0;

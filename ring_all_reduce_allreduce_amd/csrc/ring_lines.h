@@ -201,8 +201,8 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
     s_base[1] = ld_relaxed(&p.out_ctr->tail);
   }
   __syncthreads();
-  const uint64_t in_base = s_base[0];
-  const uint64_t out_base = s_base[1];
+  const uint64_t in_base = uniform64(s_base[0]);
+  const uint64_t out_base = uniform64(s_base[1]);
   const int nslots = a.nslots;
   // Per-call step counts and flags are 32-bit (a call moves far fewer than
   // 2^32 steps; flags are the low 32 bits of the 64-bit counters anyway), so
@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
         s_credit = (int)(h + (uint64_t)nslots - (out_base + nsent));
       }
       __syncthreads();
-      credit = s_credit;
+      credit = uniform32(s_credit);
       __syncthreads();
     }
     const uint32_t flag_in = in_base32 + nrecv + 1;

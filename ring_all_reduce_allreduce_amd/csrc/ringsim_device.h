@@ -167,6 +167,18 @@ __device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
 // Wait until every global load and store this thread issued has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// A value that thread 0 broadcast through LDS is the same in every lane, but
+// the compiler cannot know it: read through readfirstlane it lives in scalar
+// registers, and so do the slot addresses and buffer resources derived from
+// it. Otherwise every buffer access built on it runs in a loop over the
+// distinct resource values of the wave (which happens to run once).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int uniform32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // What a waiting thread needs to give up cleanly; kept small so that it
 // lives in registers rather than copying the kernel arguments.
 struct WaitCtx {
@@ -509,6 +521,15 @@ constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit raw da
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// The same for a p and bytes that are equal in every lane of the wave but
+// that the compiler cannot prove so: they are read from the first lane, so
+// that the resource lives in scalar registers (a resource in vector registers
+// makes the compiler wrap every access in a loop over its distinct values).
+__device__ __forceinline__ rsrc_t make_uniform_rsrc(const void* p, int64_t bytes) {
+  void* u = reinterpret_cast<void*>(uniform64(reinterpret_cast<uint64_t>(p)));
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, uniform32((int)bytes), kRsrcWord3);
 }
 
 // Instantiates L::run<DT, OP, MODE> for the runtime mode, dtype and op (the

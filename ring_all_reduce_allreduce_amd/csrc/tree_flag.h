@@ -260,8 +260,8 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
     }
   }
   __syncthreads();
-  const uint64_t in_base[2] = {s_base[0], s_base[1]};
-  const uint64_t out_base[2] = {s_base[2], s_base[3]};
+  const uint64_t in_base[2] = {uniform64(s_base[0]), uniform64(s_base[1])};
+  const uint64_t out_base[2] = {uniform64(s_base[2]), uniform64(s_base[3])};
   uint64_t head_known[2] = {out_base[0], out_base[1]};  // uniform
   uint64_t known_head[2] = {0, 0};                      // thread 0
   uint32_t in_slot[2], out_slot[2];
@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          if (j < nout) head_known[j] = s_head[j];
+          if (j < nout) head_known[j] = uniform64(s_head[j]);
         __syncthreads();
       }
     }
