@@ -44,9 +44,10 @@ WORKLOADS = {
                    desc="ring all-reduce sum, 8 simulated ranks x 64 MiB fp32 (16,777,216 elems, N(0,1)), "
                         "8 channels, 512 KiB chunks"),
     "ar8x25bf16": dict(coll="allreduce", nranks=8, count=13_107_200, dtype="bfloat16", nchannels=16,
-                       chunk_bytes=524_288, synth_workload=3, op="sum",
+                       chunk_bytes=524_288, synth_workload=3, op="sum", buckets=40,
                        desc="DDP bucket ring all-reduce sum, 8 simulated ranks x 25 MiB bf16 "
-                            "(13,107,200 elems, N(0,1e-3)), 16 channels"),
+                            "(13,107,200 elems, N(0,1e-3)), 16 channels, 40 distinct buckets back to back "
+                            "on one stream (one bucket per step)"),
     "ar16x256i32": dict(coll="allreduce", nranks=16, count=67_108_864, dtype="int32", nchannels=16,
                         chunk_bytes=524_288, synth_workload=4, op="sum",
                         desc="ring all-reduce sum, 16 simulated ranks x 256 MiB int32, 16 channels"),
@@ -246,13 +247,13 @@ def size_sweep(args) -> int:
         send = synth.device_inputs(4, n, count, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
         recv = [torch.empty_like(t) for t in send]
         for _ in range(args.warmup):
-            rs.allreduce(comm, send, recv)
+            rs.allreduce(comm, send, recv, op=args.sweep_op)
         torch.cuda.synchronize()
         idx = np.unique(np.linspace(0, count - 1, min(count, 4096)).astype(np.int64))
         cols = [t.cpu().numpy()[idx] if count <= (1 << 22) else t[torch.from_numpy(idx).cuda()].cpu().numpy()
                 for t in send]
         ok = bool(np.array_equal(recv[k % n][torch.from_numpy(idx).cuda()].cpu().numpy(),
-                                 oracle.ring_allreduce(cols, "sum", "int32", nchannels=1)[0]))
+                                 oracle.ring_allreduce(cols, args.sweep_op, "int32", nchannels=1)[0]))
         steps = args.steps if size < (64 << 20) else max(5, args.steps // 4)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -260,7 +261,7 @@ def size_sweep(args) -> int:
         torch.cuda._sleep(2_000_000)
         for i in range(steps):
             starts[i].record()
-            rs.allreduce(comm, send, recv)
+            rs.allreduce(comm, send, recv, op=args.sweep_op)
             ends[i].record()
         torch.cuda.synchronize()
         t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
@@ -269,7 +270,8 @@ def size_sweep(args) -> int:
         proto = "flag" if algo == "tree" else {1: "bulk", 2: "flag", 3: "wide"}.get(info["last_proto"], "?")
         busbw = size / t * bus_factor("allreduce", n) / 1e9
         byts = algorithmic_bytes("allreduce", n, size)
-        print(json.dumps({"nranks": n, "nchannels": nch, "bytes_per_rank": size, "algo": algo, "proto": proto,
+        print(json.dumps({"nranks": n, "nchannels": nch, "op": args.sweep_op, "bytes_per_rank": size, "algo": algo,
+                          "proto": proto,
                           "wpc": info["last_workgroups_per_channel"], "us": round(t * 1e6, 2),
                           "busbw_gbs": round(busbw, 3), "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
                           "sampled_parity": ok}), flush=True)
@@ -302,6 +304,7 @@ def main() -> int:
     ap.add_argument("--sweep-max-bytes", type=int, default=256 << 20)
     ap.add_argument("--sweep-ranks", type=int, default=16)
     ap.add_argument("--sweep-channels", type=int, default=16)
+    ap.add_argument("--sweep-op", default="sum", choices=["sum", "max"])
     ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag", "wide"])
     ap.add_argument("--algo", default="auto", choices=["auto", "ring", "tree"],
                     help="all-reduce algorithm for --sweep (auto: the library's choice)")
@@ -340,7 +343,30 @@ def main() -> int:
         return torch.from_numpy(x).to(dev)
 
     send = [upload(x) for x in xs]
-    if coll == "allreduce":
+    nbuckets = w.get("buckets", 1)
+    if coll == "allreduce" and nbuckets > 1:
+        # Distinct buckets back to back: bucket b holds base bucket b mod 5
+        # with its ranks rotated by b // 5 (the seeded inputs of 5 base
+        # buckets, shared read-only), and a receive buffer set of its own.
+        import synth
+
+        base = [send] + [[upload(x) for x in synth.rank_inputs(w["synth_workload"], n, w["count"], dtype, "normal",
+                                                                1e-3, bucket=b)] for b in range(1, 5)]
+        sends, recvs = [], []
+        for b in range(nbuckets):
+            bb, src = synth.ddp_bucket_ranks(b, n)
+            sends.append([base[bb][r] for r in src])
+            recvs.append([torch.empty_like(send[0]) for _ in range(n)])
+        per_rank_bytes = w["count"] * esize
+        bucket = [0]
+
+        def call():
+            b = bucket[0] % nbuckets
+            bucket[0] += 1
+            rs.allreduce(comm, sends[b], recvs[b], op=w["op"])
+
+        recv = recvs[0]
+    elif coll == "allreduce":
         recv = [torch.empty_like(s) for s in send]
         per_rank_bytes = w["count"] * esize
         call = lambda: rs.allreduce(comm, send, recv, op=w["op"])  # noqa: E731
@@ -364,7 +390,7 @@ def main() -> int:
     log(f"[bench] comm {json.dumps(info)}")
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1) if nbuckets > 1 else args.warmup):
         call()
     torch.cuda.synchronize()
     if rs.get_async_error(comm) != rs.SUCCESS:
@@ -452,6 +478,7 @@ def main() -> int:
             "bytes_per_rank": per_rank_bytes,
             "nchannels": w["nchannels"],
             "chunk_bytes": w["chunk_bytes"],
+            "buckets": nbuckets,
             "workgroups_per_channel": info["workgroups_per_channel"],
             "proto": {1: "bulk", 2: "flag", 3: "wide"}.get(rs.comm_query(comm)["last_proto"], "?"),
             "parallelism": "1 GPU, simulated ranks",
