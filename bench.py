@@ -169,6 +169,47 @@ def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 20.0) -> di
     }
 
 
+def mixed_copy_gbs(stream_bytes: int, resident_bytes: int, trials: int = 7) -> float:
+    """Plain copies with an all-reduce's byte mix, run concurrently on two
+    streams (bytes moved / time, median of `trials`): one copy of
+    `stream_bytes` from HBM (the user buffers' reads and writes), and
+    back-to-back copies between two 64 MiB buffers that the Infinity Cache
+    holds, moving `resident_bytes` in all (the FIFO slots' writes and
+    reads). The ceiling for the kernel's traffic on this part, with no ring,
+    no flow control and no arithmetic."""
+    import torch
+
+    big_a = torch.empty(stream_bytes // 2, dtype=torch.uint8, device="cuda")
+    big_b = torch.empty_like(big_a)
+    sm = [torch.empty(64 << 20, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    k = max(1, round(resident_bytes / (128 << 20)))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    big_b.copy_(big_a)
+    torch.cuda.synchronize()
+    rates = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d1, d2 = torch.cuda.Event(), torch.cuda.Event()
+        e0.record(cur)
+        s1.wait_event(e0)
+        s2.wait_event(e0)
+        with torch.cuda.stream(s1):
+            big_b.copy_(big_a)
+            d1.record(s1)
+        with torch.cuda.stream(s2):
+            for i in range(k):
+                sm[(i + 1) % 2].copy_(sm[i % 2])
+            d2.record(s2)
+        cur.wait_event(d1)
+        cur.wait_event(d2)
+        e1.record(cur)
+        torch.cuda.synchronize()
+        rates.append((2 * big_a.numel() + k * 2 * (64 << 20)) / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del big_a, big_b, sm
+    return statistics.median(rates)
+
+
 def d2d_copy_gbs(nbytes: int = 1 << 30, reps: int = 10, trials: int = 5) -> float:
     """Device-to-device copy (read + write bytes / time, median of `trials`
     batches of `reps` copies) as the achievable-bandwidth context of this box:
@@ -444,11 +485,12 @@ def main() -> int:
     traffic = load_traffic(args.workload, src_hash)
     d2d = d2d_copy_gbs()
     cache_copy = d2d_copy_gbs(64 << 20, reps=50)
+    mixed = mixed_copy_gbs(compulsory, bytes_alg - compulsory) if coll == "allreduce" else None
     log(f"[bench] per-launch median {t_med * 1e6:.1f} us, avg {t_avg * 1e6:.1f} us, p95 {t_p95 * 1e6:.1f} us, "
         f"CV {cv * 100:.2f}%  algBW {algbw:.1f} GB/s busBW {busbw:.1f} GB/s  "
         f"alg-bytes rate {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS * 100:.1f}% of peak)  "
         f"compulsory rate {compulsory / t_avg / 1e9:.0f} GB/s  D2D copy {d2d:.0f} GB/s "
-        f"(cache-resident {cache_copy:.0f} GB/s)")
+        f"(cache-resident {cache_copy:.0f} GB/s" + (f", this byte mix {mixed:.0f} GB/s)" if mixed else ")"))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -504,6 +546,7 @@ def main() -> int:
             "frac_compulsory": round(compulsory / t_avg / 1e9 / HBM_PEAK_GBS, 4),
             "d2d_copy_gbs": round(d2d, 1),
             "cache_resident_copy_gbs": round(cache_copy, 1),
+            "mixed_copy_gbs": round(mixed, 1) if mixed else None,
             "parity": check,
             "kernel_source_hash": src_hash,
         },
