@@ -265,9 +265,12 @@ def copy_calibration(args) -> int:
 
 
 def size_sweep(args) -> int:
-    """Latency / bandwidth of the int32 all-reduce across message sizes
-    (default 16 ranks, 16 channels); AUTO picks the algorithm and protocol per
-    size with the library's cost model, and each line reports what it ran."""
+    """Latency / bandwidth of an int32 collective across message sizes
+    (default: all-reduce, 16 ranks, 16 channels); AUTO picks the algorithm,
+    protocol and line workgroups per size with the library's cost model, and
+    each line reports what it ran. Sizes are bytes per rank: the all-reduce
+    buffer, the reduce-scatter input, the all-gather output. Each size is
+    checked against the oracle on sampled elements."""
     import numpy as np
     import torch
 
@@ -275,26 +278,51 @@ def size_sweep(args) -> int:
     import ring_all_reduce_allreduce_amd as rs
     import synth
 
+    coll = args.sweep_coll
     n, nch = args.sweep_ranks, args.sweep_channels
     comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo,
                         line_workgroups_per_channel=args.line_wpc or None)
     size = 8
     k = 0
-    while size < args.sweep_min_bytes:
+    while size < max(args.sweep_min_bytes, 4 if coll == "allreduce" else 4 * n):
         size *= 2
         k += 1
     while size <= args.sweep_max_bytes:
-        count = size // 4
-        send = synth.device_inputs(4, n, count, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
-        recv = [torch.empty_like(t) for t in send]
+        total = size // 4                                   # elements per rank of the sized buffer
+        part = total if coll == "allreduce" else total // n  # the other buffer of RS / AG
+        nin = part if coll == "all_gather" else total
+        send = synth.device_inputs(4, n, nin, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
+        recv = [torch.empty(total if coll != "reduce_scatter" else part, dtype=torch.int32, device="cuda")
+                for _ in range(n)]
+
+        def call():
+            if coll == "allreduce":
+                rs.allreduce(comm, send, recv, op=args.sweep_op)
+            elif coll == "reduce_scatter":
+                rs.reduce_scatter(comm, send, recv, op=args.sweep_op)
+            else:
+                rs.all_gather(comm, send, recv)
+
         for _ in range(args.warmup):
-            rs.allreduce(comm, send, recv, op=args.sweep_op)
+            call()
         torch.cuda.synchronize()
-        idx = np.unique(np.linspace(0, count - 1, min(count, 4096)).astype(np.int64))
-        cols = [t.cpu().numpy()[idx] if count <= (1 << 22) else t[torch.from_numpy(idx).cuda()].cpu().numpy()
-                for t in send]
-        ok = bool(np.array_equal(recv[k % n][torch.from_numpy(idx).cuda()].cpu().numpy(),
-                                 oracle.ring_allreduce(cols, args.sweep_op, "int32", nchannels=1)[0]))
+        # Sampled parity: element columns of every rank's input, reduced (or
+        # gathered) by the oracle, against the same elements of one rank's
+        # output.
+        r = k % n
+        m = part if coll != "all_gather" else nin
+        idx = np.unique(np.linspace(0, m - 1, min(m, 4096)).astype(np.int64))
+        tidx = torch.from_numpy(idx).cuda()
+        if coll == "all_gather":
+            cols = [t[tidx].cpu().numpy() for t in send]
+            want = oracle.ring_all_gather(cols, "int32", nchannels=1)[r]
+            got = np.concatenate([recv[r][b * part + tidx].cpu().numpy() for b in range(n)])
+        else:
+            off = r * part if coll == "reduce_scatter" else 0
+            cols = [t[off + tidx].cpu().numpy() for t in send]
+            want = oracle.ring_allreduce(cols, args.sweep_op, "int32", nchannels=1)[0]
+            got = recv[r][tidx].cpu().numpy()
+        ok = bool(np.array_equal(got, want))
         steps = args.steps if size < (64 << 20) else max(5, args.steps // 4)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -302,20 +330,19 @@ def size_sweep(args) -> int:
         torch.cuda._sleep(2_000_000)
         for i in range(steps):
             starts[i].record()
-            rs.allreduce(comm, send, recv, op=args.sweep_op)
+            call()
             ends[i].record()
         torch.cuda.synchronize()
         t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
         info = rs.comm_query(comm)
-        algo = {1: "ring", 2: "tree"}.get(info["last_algo"], "?")
+        algo = {1: "ring", 2: "tree"}.get(info["last_algo"], "?") if coll == "allreduce" else "ring"
         proto = "flag" if algo == "tree" else {1: "bulk", 2: "flag", 3: "wide"}.get(info["last_proto"], "?")
-        busbw = size / t * bus_factor("allreduce", n) / 1e9
-        byts = algorithmic_bytes("allreduce", n, size)
-        print(json.dumps({"nranks": n, "nchannels": nch, "op": args.sweep_op, "bytes_per_rank": size, "algo": algo,
-                          "proto": proto,
-                          "wpc": info["last_workgroups_per_channel"], "us": round(t * 1e6, 2),
-                          "busbw_gbs": round(busbw, 3), "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
-                          "sampled_parity": ok}), flush=True)
+        busbw = size / t * bus_factor(coll, n) / 1e9
+        byts = algorithmic_bytes(coll, n, size)
+        print(json.dumps({"coll": coll, "nranks": n, "nchannels": nch, "op": args.sweep_op, "bytes_per_rank": size,
+                          "algo": algo, "proto": proto, "wpc": info["last_workgroups_per_channel"],
+                          "us": round(t * 1e6, 2), "busbw_gbs": round(busbw, 3),
+                          "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4), "sampled_parity": ok}), flush=True)
         if not ok:
             return 1
         del send, recv
@@ -346,6 +373,7 @@ def main() -> int:
     ap.add_argument("--sweep-ranks", type=int, default=16)
     ap.add_argument("--sweep-channels", type=int, default=16)
     ap.add_argument("--sweep-op", default="sum", choices=["sum", "max"])
+    ap.add_argument("--sweep-coll", default="allreduce", choices=["allreduce", "reduce_scatter", "all_gather"])
     ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag", "wide"])
     ap.add_argument("--algo", default="auto", choices=["auto", "ring", "tree"],
                     help="all-reduce algorithm for --sweep (auto: the library's choice)")
