@@ -243,8 +243,7 @@ enum HostLineMode : int { kHostLinesMulti = 0, kHostLinesOne = 1, kHostLinesHalf
 
 struct LinePlan {
   int wpc;
-  int mode;       // HostLineMode
-  int64_t steps;  // slot steps of the longest unit part
+  int mode;  // HostLineMode
 };
 
 // The line kernel a launch with `wpc` workgroups per channel needs: the
@@ -258,7 +257,7 @@ LinePlan line_plan(const RingArgs& a, int mode, int esize, int line_proto, int d
   const int64_t slot_lines = line_slot_bytes(wpc) / 16;
   const int64_t lines = std::min(unit_lines, slot_lines);
   const int m = lines <= kThreads / 2 ? kHostLinesHalf : lines <= kThreads ? kHostLinesOne : kHostLinesMulti;
-  return LinePlan{wpc, m, div_up(unit_lines, slot_lines)};
+  return LinePlan{wpc, m};
 }
 
 bool line_plan_resident(const ringsim_comm* c, const LinePlan& lp) {
@@ -326,7 +325,7 @@ ProtoChoice pick_proto(const ringsim_comm* c, int mode, size_t count, int dtype)
   auto bulk = [&]() {
     ProtoChoice pc;
     pc.proto = RINGSIM_PROTO_BULK;
-    pc.plan = LinePlan{c->wpc, kHostLinesMulti, 0};
+    pc.plan = LinePlan{c->wpc, kHostLinesMulti};
     pc.us = bulk_model_us(RingModel(), mode, c->nranks, bytes);
     return pc;
   };
