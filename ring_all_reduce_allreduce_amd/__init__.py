@@ -212,43 +212,58 @@ def comm_query(comm: Comm) -> dict:
     return info.as_dict()
 
 
-def _dtype_name(t) -> str:
-    import torch
+_TORCH_DTYPES: dict | None = None
 
-    m = {torch.int32: "int32", torch.int64: "int64", torch.float32: "float32", torch.bfloat16: "bfloat16"}
-    if t.dtype not in m:
+
+def _dtype_name(t) -> str:
+    global _TORCH_DTYPES
+    if _TORCH_DTYPES is None:
+        import torch
+
+        _TORCH_DTYPES = {torch.int32: "int32", torch.int64: "int64", torch.float32: "float32",
+                         torch.bfloat16: "bfloat16"}
+    name = _TORCH_DTYPES.get(t.dtype)
+    if name is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return m[t.dtype]
+    return name
 
 
 def _ptr_array(bufs: Sequence) -> ctypes.Array:
-    arr = (ctypes.c_void_p * len(bufs))()
-    for k, b in enumerate(bufs):
-        arr[k] = b if isinstance(b, int) else b.data_ptr()
-    return arr
+    return (ctypes.c_void_p * len(bufs))(*[b if isinstance(b, int) else b.data_ptr() for b in bufs])
 
 
 def _marshal(comm: Comm, sendbufs, recvbufs, dtype):
     if len(sendbufs) != comm.nranks or len(recvbufs) != comm.nranks:
         raise ValueError(f"need {comm.nranks} send and receive buffers")
     if dtype is None:
-        if isinstance(sendbufs[0], int):
+        first = sendbufs[0]
+        if isinstance(first, int):
             raise ValueError("dtype is required with raw pointers")
-        dtype = _dtype_name(sendbufs[0])
-        for b in list(sendbufs) + list(recvbufs):
-            if not isinstance(b, int):
-                if _dtype_name(b) != dtype:
-                    raise TypeError("all buffers must share one dtype")
-                if not b.is_cuda:
-                    raise ValueError("buffers must be device tensors")
+        dtype = _dtype_name(first)
+        tdt = first.dtype
+        for bufs in (sendbufs, recvbufs):
+            for b in bufs:
+                if not isinstance(b, int):
+                    if b.dtype != tdt:
+                        raise TypeError("all buffers must share one dtype")
+                    if not b.is_cuda:
+                        raise ValueError("buffers must be device tensors")
     return _ptr_array(sendbufs), _ptr_array(recvbufs), DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _current_stream() -> int:
+    """The current HIP stream of the current device, as an integer handle."""
     import torch
 
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(_current_stream())
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
