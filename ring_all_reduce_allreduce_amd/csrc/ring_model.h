@@ -17,17 +17,20 @@
 // and the kernel sustains ~6.9 TB/s.
 //
 // Line protocols (FLAG, WIDE): a workgroup moves its part of every stage in
-// steps of at most one slot, and its speed is set by steps, not bytes. The
-// first step of every stage waits for the neighbour's previous stage (a hop);
-// further steps of the same stage find their lines already written and cost
-// a step time. Both grow with the lines of a step (lines per thread), and
-// both grow when more workgroups than compute units share the device:
+// steps of at most one slot, and up to a few MiB its speed is set by steps,
+// not bytes. The first step of every stage waits for the neighbour's previous
+// stage (a hop); further steps of the same stage find their lines already
+// written and cost a step time. Both grow with the lines of a step (lines per
+// thread), and both grow when more workgroups than compute units share the
+// device. Large messages meet the line protocols' byte rate instead:
 //
-//   t = base + crowd * (hops * hop(L) + stages * (steps - 1) * step(L))
+//   steps_us = crowd * (hops * hop(L) + stages * (steps - 1) * step(L))
+//   t = base + sqrt(steps_us^2 + (line_bytes / line_bandwidth)^2)
 //
 // with L the lines of a workgroup's step, steps the slot steps of one stage
 // of one workgroup (all loops), hop(L) = a + b * L / 256, step(L) likewise,
-// crowd = 1 + c * (workgroups / CUs - 1) above one workgroup per CU. The
+// crowd = 1 + c * (workgroups / CUs - 1) above one workgroup per CU, and
+// line_bytes the method bytes with the line format's FIFO factor. The
 // constants are fitted to bench.py sweeps on MI355X (4, 8 and 16 ranks with
 // as many channels, 1, 2, 4 and 8 workgroups per channel, 4 KiB .. 8 MiB per
 // rank); the library evaluates every workgroup count it may launch and takes
@@ -48,10 +51,11 @@ struct RingModel {
   double bulk_gbs = 6900.0;
   // Line protocols, [FLAG, WIDE][a, b]: per hop and per further step,
   // a + b * lines / 256 microseconds.
-  double line_base_us = 6.45;
-  double line_hop_us[2][2] = {{0.700, 0.631}, {0.795, 0.341}};
-  double line_step_us[2][2] = {{1.005, 0.103}, {0.953, 0.097}};
-  double line_crowd = 0.515;
+  double line_base_us = 6.83;
+  double line_hop_us[2][2] = {{0.727, 0.400}, {0.822, 0.170}};
+  double line_step_us[2][2] = {{0.971, 0.097}, {0.888, 0.095}};
+  double line_crowd = 0.368;
+  double line_gbs = 4540.0;
   // Double-binary tree (flag lines): per-hop latency, per-workgroup rate of
   // the ring-equivalent flag bytes, and the tree's ceiling.
   double tree_hop_us = 1.25;
@@ -110,7 +114,9 @@ inline double line_model_us(const RingModel& m, int coll, int nranks, int nchann
   const double crowd = 1.0 + m.line_crowd * std::max(0.0, wgs / sh.cus - 1.0);
   const double hop = m.line_hop_us[k][0] + m.line_hop_us[k][1] * lines / 256.0;
   const double step = m.line_step_us[k][0] + m.line_step_us[k][1] * lines / 256.0;
-  return m.line_base_us + crowd * (hops * hop + (hops + 1.0) * (steps - 1.0) * step);
+  const double steps_us = crowd * (hops * hop + (hops + 1.0) * (steps - 1.0) * step);
+  const double bytes = model_bytes(coll, nranks, bytes_per_rank, proto);
+  return m.line_base_us + std::hypot(steps_us, bytes / (m.line_gbs * 1e3));
 }
 
 // Predicted microseconds of a double-binary-tree all-reduce: the reduce

@@ -202,7 +202,7 @@ int model_proto(int proto) {
 // Fills the protocol-dependent launch geometry; line_wpc is the workgroup
 // count of a line launch (1, 2, 4 or 8). The flag FIFO holds one array per
 // count, in increasing order, each [rank][channel][part][slot] with
-// kFlagSlots slots of line_slot_bytes(count) per part.
+// kFlagSlots slots of kFlagSlotBytes per part.
 void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int line_wpc = 1) {
   a->chunk = (int64_t)c->chunk_bytes / esize;
   if (proto == RINGSIM_PROTO_FLAG || proto == RINGSIM_PROTO_WIDE) {
@@ -214,7 +214,7 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int li
     a->fifo_stride = c->nchannels * line_wpc;
     a->fifo_mul = line_wpc;
     a->nslots = kFlagSlots;
-    a->slot_bytes = line_slot_bytes(line_wpc);
+    a->slot_bytes = kFlagSlotBytes;
     a->group = kLineGroupSteps;
   } else {
     a->wpc = c->wpc;
@@ -254,7 +254,7 @@ LinePlan line_plan(const RingArgs& a, int mode, int esize, int line_proto, int d
   RingArgs t = a;
   t.wpc = wpc;
   const int64_t unit_lines = div_up(max_unit_bytes(t, mode, esize), payload);
-  const int64_t slot_lines = line_slot_bytes(wpc) / 16;
+  const int64_t slot_lines = kFlagSlotBytes / 16;
   const int64_t lines = std::min(unit_lines, slot_lines);
   const int m = lines <= kThreads / 2 ? kHostLinesHalf : lines <= kThreads ? kHostLinesOne : kHostLinesMulti;
   return LinePlan{wpc, m};
@@ -301,7 +301,7 @@ ProtoChoice pick_line(const ringsim_comm* c, const RingArgs& a, int mode, int dt
     if (w > 1 && (!line_plan_resident(c, plan) || (!c->line_wpc_cfg && nc * w > 2 * (int64_t)c->compute_units)))
       continue;
     const LineShape sh{w, lp == kLineWide && dtype != RINGSIM_INT64 ? 12.0 : 8.0,
-                       (double)(line_slot_bytes(w) / 16), (double)c->chunk_bytes, c->compute_units};
+                       (double)(kFlagSlotBytes / 16), (double)c->chunk_bytes, c->compute_units};
     const double us = line_model_us(m, mode, c->nranks, c->nchannels, bytes, model_proto(proto), sh);
     // A configured count is taken as the most that may run, not a hint.
     if (best.us < 0.0 || (c->line_wpc_cfg ? w > best.plan.wpc : us < best.us)) {
@@ -824,7 +824,7 @@ ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t
     double best = -1.0;
     for (int w = 1; w <= kMaxLineWpc; w *= 2) {
       if (w > 1 && (int64_t)nranks * nchannels * w > 2 * 256) break;
-      const LineShape sh{w, k ? 12.0 : 8.0, (double)(line_slot_bytes(w) / 16), 524288.0, 256};
+      const LineShape sh{w, k ? 12.0 : 8.0, (double)(kFlagSlotBytes / 16), 524288.0, 256};
       const double us = line_model_us(m, coll, nranks, nchannels, b, proto, sh);
       if (best < 0.0 || us < best) best = us;
     }

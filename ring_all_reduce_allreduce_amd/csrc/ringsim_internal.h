@@ -21,17 +21,12 @@ constexpr int kFlagHeadEvery = kFlagSlots / 2;  // line protocols publish head e
 // neighbours sit in stage 0 (the rest may hold drained but unpublished steps).
 constexpr int kLineGroupSteps = kFlagSlots - kFlagHeadEvery;
 // Line launches split each (rank, channel) over 1, 2, 4 or 8 workgroups;
-// each count has a FIFO array of its own: kFlagSlots slots per workgroup, of
-// kFlagSlotBytes with one workgroup per channel and 8 KiB (512 lines) with
-// more.
+// each count has a FIFO array of its own, kFlagSlots slots of kFlagSlotBytes
+// per workgroup.
 constexpr int kLineWpcLevels = 4;
 constexpr int kMaxLineWpc = 1 << (kLineWpcLevels - 1);
-constexpr int kLineSplitSlotBytes = 8192;
-__host__ __device__ constexpr int line_slot_bytes(int wpc) { return wpc > 1 ? kLineSplitSlotBytes : kFlagSlotBytes; }
 // Bytes of the FIFO array of one workgroup count, per (rank, channel).
-__host__ __device__ constexpr int64_t line_level_bytes(int wpc) {
-  return (int64_t)wpc * kFlagSlots * line_slot_bytes(wpc);
-}
+__host__ __device__ constexpr int64_t line_level_bytes(int wpc) { return (int64_t)wpc * kFlagSlots * kFlagSlotBytes; }
 
 // Line formats of the flag-packed protocols (16 bytes per line).
 enum LineProto : int { kLineFlag = 0, kLineWide = 1 };
