@@ -75,13 +75,18 @@ def test_call_returns_before_completion_and_keeps_stream_order():
         rs.comm_destroy(comm)
 
 
-@pytest.mark.parametrize("proto", ["bulk", "flag", "wide"])
+@pytest.mark.parametrize("proto", ["bulk", "flag", "wide", "flag4", "wide4"])
 def test_missing_rank_times_out_and_poisons_the_comm(proto, monkeypatch):
+    """Every workgroup of rank 2 returns at once; its neighbours' bounded waits
+    expire (line launches also with four workgroups per channel), the kernel
+    ends and the comm reports the error on the next call."""
     import torch
 
     monkeypatch.setenv("RINGSIM_DEBUG_SKIP_RANK", "2")
     n, count = 4, 200_000 if proto == "bulk" else 1000
-    comm = rs.comm_init(n, 2, proto, timeout_ms=50)
+    extra = {"line_workgroups_per_channel": 4} if proto.endswith("4") else {}
+    proto = proto[:-1] if proto.endswith("4") else proto
+    comm = rs.comm_init(n, 2, proto, timeout_ms=50, **extra)
     monkeypatch.delenv("RINGSIM_DEBUG_SKIP_RANK")
     try:
         send = [torch.ones(count, device="cuda:0") for _ in range(n)]
