@@ -60,8 +60,9 @@ WORKLOADS = {
                         chunk_bytes=524_288, synth_workload=5, op="sum",
                         desc="ring all-gather, 8 simulated ranks x 16 MiB bf16 in, 128 MiB out"),
     "a2a8x32bf16": dict(coll="alltoall", nranks=8, count=16_777_216, dtype="bfloat16", nchannels=1,
-                        chunk_bytes=524_288, synth_workload=5, op="sum",
-                        desc="all-to-all, 8 simulated ranks x 8 chunks of 512x4096 bf16 (32 MiB per rank)"),
+                        chunk_bytes=524_288, synth_workload=5, op="sum", buffer_sets=4,
+                        desc="all-to-all, 8 simulated ranks x 8 chunks of 512x4096 bf16 (32 MiB per rank); "
+                             "4 buffer sets in turn, so that no step finds its input in the Infinity Cache"),
 }
 DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32", "int64": "i64"}
 
@@ -450,9 +451,19 @@ def main() -> int:
         per_rank_bytes = w["count"] * esize
         call = lambda: rs.all_gather(comm, send, recv)  # noqa: E731
     else:
-        recv = [torch.empty_like(s) for s in send]
+        # Distinct buffer sets in turn (1 GiB of inputs for 4 sets): a step
+        # never reads what the previous step left in the 256 MB cache.
+        nsets = w.get("buffer_sets", 1)
+        sends = [send] + [[t.clone() for t in send] for _ in range(nsets - 1)]
+        recvs = [[torch.empty_like(t) for t in send] for _ in range(nsets)]
+        recv = recvs[0]
         per_rank_bytes = xs[0].shape[0] * esize
-        call = lambda: rs.alltoall(comm, send, recv)  # noqa: E731
+        step = [0]
+
+        def call():
+            b = step[0] % nsets
+            step[0] += 1
+            rs.alltoall(comm, sends[b], recvs[b])
 
     comm = rs.comm_init(n, w["nchannels"], "auto", chunk_bytes=w["chunk_bytes"],
                         workgroups_per_channel=args.wpc or None, slot_bytes=args.slot_bytes or None,
@@ -461,7 +472,7 @@ def main() -> int:
     log(f"[bench] comm {json.dumps(info)}")
 
     stream = torch.cuda.current_stream()
-    for _ in range(max(args.warmup, 1) if nbuckets > 1 else args.warmup):
+    for _ in range(max(args.warmup, 1) if nbuckets > 1 or w.get("buffer_sets", 1) > 1 else args.warmup):
         call()
     torch.cuda.synchronize()
     if rs.get_async_error(comm) != rs.SUCCESS:
@@ -551,6 +562,7 @@ def main() -> int:
             "nchannels": w["nchannels"],
             "chunk_bytes": w["chunk_bytes"],
             "buckets": nbuckets,
+            "buffer_sets": w.get("buffer_sets", 1),
             "workgroups_per_channel": info["workgroups_per_channel"],
             "proto": {1: "bulk", 2: "flag", 3: "wide"}.get(rs.comm_query(comm)["last_proto"], "?"),
             "parallelism": "1 GPU, simulated ranks",

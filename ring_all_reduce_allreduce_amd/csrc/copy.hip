@@ -1,63 +1,88 @@
 // copy.hip -- all-to-all as a block transpose, and one-rank local copies.
+#include <algorithm>
+
 #include "ringsim_device.h"
 
 namespace ringsim {
+
+constexpr int64_t kCopyWorkgroups = 1024;
 
 // ---------------------------------------------------------------------------
 // Copy kernel: all-to-all blocks, or one-rank local copies
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
-  const int blk = blockIdx.y;
-  int src_rank, dst_rank;
-  int64_t src_off = 0, dst_off = 0;
+// Block b of the launch: all-to-all block (source rank, destination rank) =
+// (b mod N, b / N), read at the destination's offset in the source buffer
+// and written at the source's offset in the destination buffer; or, for local
+// copies, rank b's whole buffer.
+struct CopyBlock {
+  const char* src;
+  char* dst;
+};
+
+__device__ __forceinline__ CopyBlock copy_block(const CopyArgs& a, int b) {
   if (a.transpose) {
-    dst_rank = blk / a.nranks;
-    src_rank = blk - dst_rank * a.nranks;
-    src_off = (int64_t)dst_rank * a.block_bytes;
-    dst_off = (int64_t)src_rank * a.block_bytes;
-  } else {
-    src_rank = dst_rank = blk;
+    const int d = b / a.nranks, s = b - d * a.nranks;
+    return CopyBlock{a.src[s] + (int64_t)d * a.block_bytes, a.dst[d] + (int64_t)s * a.block_bytes};
   }
-  const char* src = a.src[src_rank] + src_off;
-  char* dst = a.dst[dst_rank] + dst_off;
+  return CopyBlock{a.src[b], a.dst[b]};
+}
+
+// The workgroups walk the tiles of all blocks with one stride (a flat grid of
+// a few per compute unit beats one grid row per block: every workgroup keeps
+// streaming instead of finishing its block early). A tile is 256 threads x 8
+// vectors of 16 bytes, non-temporal both ways (each byte is touched once).
+__global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
+  const int nblk = a.transpose ? a.nranks * a.nranks : a.nranks;
   const int tid = threadIdx.x;
+  int64_t nv = 0;  // whole vectors per block
   if (a.vec_ok) {
-    const int64_t nv = a.block_bytes / 16;
-    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
-    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
-    const int64_t tile = (int64_t)kThreads * kUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * tile; base < nv; base += (int64_t)gridDim.x * tile) {
+    nv = a.block_bytes / 16;
+    constexpr int64_t kTile = (int64_t)kThreads * kUnroll;
+    const int64_t per_block = div_up(nv, kTile);
+    const int64_t total = per_block * nblk;
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+      const int b = (int)(t / per_block);
+      const int64_t base = (t - (int64_t)b * per_block) * kTile;
+      const CopyBlock cb = copy_block(a, b);
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(cb.src) + base;
+      u32x4* d4 = reinterpret_cast<u32x4*>(cb.dst) + base;
       u32x4 v[kUnroll];
+      if (base + kTile <= nv) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads + tid;
-        if (i < nv) v[u] = __builtin_nontemporal_load(s4 + i);
-      }
+        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(s4 + u * kThreads + tid);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads + tid;
-        if (i < nv) __builtin_nontemporal_store(v[u], d4 + i);
+        for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], d4 + u * kThreads + tid);
+      } else {
+        const int64_t left = nv - base;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          if (u * kThreads + tid < left) v[u] = __builtin_nontemporal_load(s4 + u * kThreads + tid);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          if (u * kThreads + tid < left) __builtin_nontemporal_store(v[u], d4 + u * kThreads + tid);
       }
     }
-    for (int64_t i = nv * 16 + (int64_t)blockIdx.x * kThreads + tid; i < a.block_bytes;
-         i += (int64_t)gridDim.x * kThreads)
-      dst[i] = src[i];
-  } else {
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.block_bytes; i += (int64_t)gridDim.x * kThreads)
-      dst[i] = src[i];
+  }
+  // Bytes past the last whole vector of every block (all of them when the
+  // buffers are not 16-byte aligned).
+  const int64_t rest = a.block_bytes - nv * 16;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < rest * nblk; i += (int64_t)gridDim.x * kThreads) {
+    const int b = (int)(i / rest);
+    const CopyBlock cb = copy_block(a, b);
+    const int64_t off = nv * 16 + (i - (int64_t)b * rest);
+    cb.dst[off] = cb.src[off];
   }
 }
 
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
-  const int nblocks = a.transpose ? a.nranks * a.nranks : a.nranks;
-  const int64_t tile = a.vec_ok ? (int64_t)kThreads * kUnroll * 16 : (int64_t)kThreads;
-  int64_t tiles = div_up(a.block_bytes, tile);
-  const int64_t cap = max64(1, 4096 / nblocks);
-  if (tiles > cap) tiles = cap;
-  if (tiles < 1) tiles = 1;
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)tiles, (unsigned)nblocks), dim3(kThreads), 0, s, a);
+  const int nblk = a.transpose ? a.nranks * a.nranks : a.nranks;
+  const int64_t per_block = a.vec_ok ? div_up(a.block_bytes / 16, (int64_t)kThreads * kUnroll)
+                                     : div_up(a.block_bytes, (int64_t)kThreads);
+  // About four workgroups per compute unit, never more than there are tiles.
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(kCopyWorkgroups, per_block * nblk));
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
