@@ -96,6 +96,8 @@ typedef enum {
  * of every line is payload). WIDE packs one 4-byte flag with 12 bytes of
  * payload in each 16-byte line (8 bytes for int64), written and read as one
  * 128-bit access: the MI355X counterpart of LL128, for medium messages.
+ * FLAG and WIDE launches split every (rank, channel) over 1, 2, 4 or 8
+ * workgroups, chosen per call (line_workgroups_per_channel caps it).
  * AUTO picks the protocol with the lowest predicted time
  * (ringsim_debug_model), or FLAG below flag_threshold_bytes per rank and
  * BULK above it when a threshold is configured. Every protocol walks the
@@ -247,10 +249,14 @@ const char* ringsim_get_error_string(ringsim_result_t result);
 /* Host-only cost model behind AUTO ("NCCL" book, ch. 5, ring.cc: latency =
  * hops x per-hop latency, bandwidth term = bytes moved / achievable bandwidth,
  * the FIFO bytes scaled by each line format: x2 for FLAG, x4/3 for WIDE),
- * with constants measured on MI355X. Writes the predicted microseconds of one
- * call of `coll` (RINGSIM_COLL_ALLREDUCE, _REDUCE_SCATTER or _ALL_GATHER)
- * with `bytes_per_rank` bytes per rank (all-reduce buffer, reduce-scatter
- * input, all-gather output) on each protocol. Touches no device. */
+ * with constants measured on MI355X. BULK: hops and bytes; FLAG and WIDE:
+ * the slot steps of one workgroup (each costing more the more lines it
+ * holds) and the line bytes, at the workgroup count per channel (1, 2, 4 or
+ * 8, at most two workgroups per compute unit of a 256-CU device) that the
+ * model finds fastest. Writes the predicted microseconds of one call of
+ * `coll` (RINGSIM_COLL_ALLREDUCE, _REDUCE_SCATTER or _ALL_GATHER) with
+ * `bytes_per_rank` bytes per rank (all-reduce buffer, reduce-scatter input,
+ * all-gather output) on each protocol. Touches no device. */
 ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t bytes_per_rank, double* us_bulk,
                                      double* us_flag, double* us_wide);
 
