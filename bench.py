@@ -41,6 +41,10 @@ COPY_KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("copy.hip", "ringsim_int
 # Named single-GPU workloads. "ar8x64" is the headline; the others exist for
 # exploration and print the same JSON fields.
 WORKLOADS = {
+    "ar4x4k": dict(coll="allreduce", nranks=4, count=1024, dtype="float32", nchannels=1,
+                   chunk_bytes=524_288, synth_workload=1, op="sum", proto="bulk",
+                   desc="ring all-reduce sum, 4 simulated ranks x 1024 fp32 (integers in [-8, 8]), 1 channel, "
+                        "bulk protocol (latency-bound: report us per call)"),
     "ar8x64": dict(coll="allreduce", nranks=8, count=16_777_216, dtype="float32", nchannels=8,
                    chunk_bytes=524_288, synth_workload=2, op="sum",
                    desc="ring all-reduce sum, 8 simulated ranks x 64 MiB fp32 (16,777,216 elems, N(0,1)), "
@@ -465,7 +469,7 @@ def main() -> int:
             step[0] += 1
             rs.alltoall(comm, sends[b], recvs[b])
 
-    comm = rs.comm_init(n, w["nchannels"], "auto", chunk_bytes=w["chunk_bytes"],
+    comm = rs.comm_init(n, w["nchannels"], w.get("proto", "auto"), chunk_bytes=w["chunk_bytes"],
                         workgroups_per_channel=args.wpc or None, slot_bytes=args.slot_bytes or None,
                         nslots=args.nslots or None)
     info = rs.comm_query(comm)
