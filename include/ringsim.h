@@ -118,7 +118,10 @@ typedef enum {
  * reducing one half of the buffer up to its root and broadcasting the result
  * back down. Tree 1 takes elements [h, count) with
  * h = min(count, alignUp(ceil(count/2), 16/elemsize)); a rank folds its own
- * data, then its first child's partial, then its second child's. The tree
+ * data, then its first child's partial, then its second child's. Each half
+ * is split over channels of one 2 KiB slice (one 16-byte flag line per
+ * thread) each, as many as allow one tree workgroup per compute unit
+ * (4 x N x channels <= CUs); longer channels pipeline slice by slice. The tree
  * always moves flag-packed lines and needs 2*log2(N) dependent hops instead
  * of the ring's 2(N-1). AUTO takes the tree only where the fold order cannot
  * change a result bit (integer types, and max/min of any type) and the cost
@@ -171,7 +174,7 @@ typedef struct {
   uint64_t calls;              /* collective calls enqueued so far */
   int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG/WIDE, 0 if none */
   int algo;                    /* configured all-reduce algorithm (ringsim_algo_t) */
-  int tree_channels;           /* most channels per tree an all-reduce may use */
+  int tree_channels;           /* channels per tree in the tree FIFOs; a call takes at most CUs / (4N) */
   size_t tree_fifo_bytes;      /* double-tree FIFO bytes in HBM */
   int last_algo;               /* algorithm of the latest all-reduce: RINGSIM_ALGO_RING/TREE, 0 if none */
   int line_max_workgroups_per_channel; /* most workgroups per channel a FLAG/WIDE launch may take */
@@ -266,9 +269,11 @@ ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t
 ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
 
 /* Host-only cost model of the tree all-reduce with `tree_channels` channels
- * per tree and `bytes_per_rank` bytes per rank: base + 2 x tree depth x the
- * flag protocol's hop latency + the flag protocol's bytes over the bandwidth
- * of the workgroups that move them. Writes the predicted microseconds. */
+ * per tree and `bytes_per_rank` bytes per rank on a 256-CU device: base +
+ * 2 x tree depth x the per-hop latency of one slice (one 16-byte flag line
+ * per thread) + the load of the tree's workgroups on the compute units + one
+ * further step per further slice of a channel. Writes the predicted
+ * microseconds. */
 ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us);
 
 /* Host-only view of the partition used by the kernels. For `coll`

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libringsim.so")
 SOURCES = ["ringsim_api.hip", "ring_bulk.hip", "ring_lines_half.hip", "ring_lines_one.hip", "ring_lines_multi.hip",
-           "tree_one.hip", "tree_multi.hip", "copy.hip"]
+           "tree.hip", "copy.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.

@@ -356,15 +356,23 @@ ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void*
   return RINGSIM_SUCCESS;
 }
 
-// Tree channels for one all-reduce: enough that each workgroup moves at
-// least kTreeChannelBytes of the half buffer its tree owns.
-constexpr size_t kTreeChannelBytes = 16384;
+// Tree channels of one all-reduce: one slice (one line per thread) of the
+// half buffer its tree owns per channel, and at most one tree workgroup per
+// compute unit: with more, the steps of the workgroups that share a unit
+// queue behind each other and a longer pipeline per channel is faster.
+constexpr int64_t kTreeSliceBytes = kTreeSlotBytes / 2;
 
 int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank) {
-  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), (int64_t)kTreeChannelBytes);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, c->tree_channels));
+  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), kTreeSliceBytes);
+  const int64_t per_cu_cap = std::max<int64_t>(1, c->compute_units / (4 * (int64_t)c->nranks));
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, per_cu_cap, (int64_t)c->tree_channels}));
 }
 
+double tree_predict_us(const ringsim_comm* c, size_t bytes_per_rank) {
+  const RingModel m;
+  return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank), (double)kTreeSliceBytes,
+                       (double)bytes_per_rank, c->compute_units);
+}
 
 // AUTO's algorithm: the tree only where the fold order cannot show in the
 // result (integers wrap associatively; max/min pick one input), only when
@@ -374,10 +382,7 @@ bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t count) {
   const bool order_free = dtype == RINGSIM_INT32 || dtype == RINGSIM_INT64 || op == RINGSIM_MAX || op == RINGSIM_MIN;
   const bool lines_ok = c->proto == RINGSIM_PROTO_AUTO || c->proto == RINGSIM_PROTO_FLAG;
   if (!order_free || !lines_ok || c->tree_channels < 1) return false;
-  const RingModel m;
-  const size_t bytes_per_rank = count * (size_t)dtype_size(dtype);
-  return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank), (double)bytes_per_rank) <
-         pick_proto(c, kAllReduce, count, dtype).us;
+  return tree_predict_us(c, count * (size_t)dtype_size(dtype)) < pick_proto(c, kAllReduce, count, dtype).us;
 }
 
 ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const* rb, size_t count, int dtype,
@@ -404,11 +409,7 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   a.host_abort = c->host_words_dev;
   a.host_err = c->host_words_dev + 1;
   a.timeout_ticks = c->timeout_ticks;
-  // The longest slice of the launch: tree 0 takes the larger half.
-  const int64_t A = 16 / dtype_size(dtype);
-  const int64_t longest = std::min<int64_t>(a.slot_bytes / 2, channel_span(tree_split(a.count, A), a.nchannels, A) *
-                                                                 dtype_size(dtype));
-  const hipError_t e = longest <= (int64_t)kThreads * 8 ? launch_tree_one(a, dtype, op, s) : launch_tree_multi(a, dtype, op, s);
+  const hipError_t e = launch_tree_kernel(a, dtype, op, s);
   if (e != hipSuccess) {
     RS_LOG(kLogWarn, "tree kernel launch failed: %s", hipGetErrorString(e));
     return RINGSIM_UNHANDLED_DEVICE_ERROR;
@@ -587,7 +588,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
 
   // Tree channels: every workgroup of a tree launch (4 per rank and channel)
   // must be resident at once, like the ring's.
-  const int tree_per_cu = std::min(tree_one_blocks_per_cu(), tree_multi_blocks_per_cu());
+  const int tree_per_cu = tree_blocks_per_cu();
   const int64_t tree_resident = (int64_t)tree_per_cu * cus;
   const int tree_channels = nranks < 2 ? 0 : (int)std::min<int64_t>(nchannels, tree_resident / (4 * (int64_t)nranks));
   if (cfg.algo == RINGSIM_ALGO_TREE && nranks > 1 && tree_channels < 1) return RINGSIM_INVALID_USAGE;
@@ -849,7 +850,9 @@ ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t 
   if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || tree_channels < 1 || tree_channels > RINGSIM_MAX_CHANNELS || !us)
     return RINGSIM_INVALID_ARGUMENT;
   const RingModel m;
-  *us = tree_model_us(m, nranks, double_tree_depth(nranks), tree_channels, (double)bytes_per_rank);
+  // A 256-CU device, as the ring model above.
+  *us = tree_model_us(m, nranks, double_tree_depth(nranks), tree_channels, (double)kTreeSliceBytes,
+                      (double)bytes_per_rank, 256);
   return RINGSIM_SUCCESS;
 }
 

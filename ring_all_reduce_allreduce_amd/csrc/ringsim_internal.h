@@ -87,7 +87,7 @@ struct TreeArgs {
   int nchannels;        // tree channels of this launch (<= ch_stride)
   int ch_stride;        // tree channels in the FIFO and counter arrays
   int nslots;
-  int slot_bytes;       // flag slot: half of it is payload
+  int slot_bytes;       // kTreeSlotBytes: one flag line per thread, half of it payload
   int head_every;       // consumers publish `head` every this many steps
   int vec_ok;
   int skip_rank;
@@ -101,7 +101,10 @@ struct TreeArgs {
 };
 
 constexpr int kTreeSlots = 8;
-constexpr int kTreeSlotBytes = kFlagSlotBytes;
+// One 16-byte line per thread: every step of a tree workgroup is a single
+// load, fold and store per thread, the shortest path from a child's flag to
+// the parent's store.
+constexpr int kTreeSlotBytes = kThreads * 16;
 
 struct CopyArgs {
   const char* src[RINGSIM_MAX_RANKS];
@@ -113,7 +116,7 @@ struct CopyArgs {
 };
 
 // Kernel launchers (ring_bulk.hip, ring_lines_half.hip, ring_lines_one.hip,
-// ring_lines_multi.hip, tree_one.hip, tree_multi.hip, copy.hip).
+// ring_lines_multi.hip, tree.hip, copy.hip).
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 // Line protocols: the _half variant when no step of the launch holds more
 // than 128 lines, _one when none holds more than 256, else _multi.
@@ -121,14 +124,11 @@ hipError_t launch_ring_lines_half(const RingArgs& a, int line_proto, int mode, i
 hipError_t launch_ring_lines_one(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_lines_multi(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
-// Double-binary tree: the _one variant when no slice of the launch holds more
-// than one line per thread, else _multi.
-hipError_t launch_tree_one(const TreeArgs& a, int dtype, int op, hipStream_t s);
-hipError_t launch_tree_multi(const TreeArgs& a, int dtype, int op, hipStream_t s);
+// Double-binary tree: one slot (one line per thread) per step.
+hipError_t launch_tree_kernel(const TreeArgs& a, int dtype, int op, hipStream_t s);
 // Max co-resident workgroups per CU over every instantiation of a kernel
 // family (the bulk kernels launched with `lds_bytes` of dynamic LDS).
-int tree_one_blocks_per_cu();
-int tree_multi_blocks_per_cu();
+int tree_blocks_per_cu();
 int bulk_blocks_per_cu(size_t lds_bytes);
 int line_half_blocks_per_cu();
 int line_one_blocks_per_cu();

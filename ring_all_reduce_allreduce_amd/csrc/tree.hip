@@ -1,5 +1,4 @@
-// tree_one.hip -- instantiations of the double-binary-tree kernel for
-// slices of at most one line per thread (small messages).
+// tree.hip -- instantiations and launch of the double-binary-tree kernel.
 #include "tree_flag.h"
 
 namespace ringsim {
@@ -10,10 +9,10 @@ template <int DT>
 hipError_t tree_dispatch_op(const TreeArgs& a, int op, hipStream_t s) {
   const int grid = a.nranks * 2 * a.nchannels * 2;
   switch (op) {
-    case RINGSIM_SUM: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_SUM, true>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case RINGSIM_PROD: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_PROD, true>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case RINGSIM_MAX: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_MAX, true>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case RINGSIM_MIN: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_MIN, true>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case RINGSIM_SUM: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_SUM>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case RINGSIM_PROD: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_PROD>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case RINGSIM_MAX: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_MAX>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case RINGSIM_MIN: hipLaunchKernelGGL((tree_flag_kernel<DT, RINGSIM_MIN>), dim3(grid), dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -21,7 +20,7 @@ hipError_t tree_dispatch_op(const TreeArgs& a, int op, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_tree_one(const TreeArgs& a, int dtype, int op, hipStream_t s) {
+hipError_t launch_tree_kernel(const TreeArgs& a, int dtype, int op, hipStream_t s) {
   switch (dtype) {
     case RINGSIM_INT32: return tree_dispatch_op<RINGSIM_INT32>(a, op, s);
     case RINGSIM_INT64: return tree_dispatch_op<RINGSIM_INT64>(a, op, s);
@@ -31,14 +30,14 @@ hipError_t launch_tree_one(const TreeArgs& a, int dtype, int op, hipStream_t s) 
   }
 }
 
-int tree_one_blocks_per_cu() {
+int tree_blocks_per_cu() {
   int m = 1 << 30;
   auto acc = [&](int v) { m = v < m ? v : m; };
 #define RS_TREE_OCC_DT(DT)                                         \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_SUM, true>, 0));      \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_PROD, true>, 0));     \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_MAX, true>, 0));      \
-  acc(occupancy(tree_flag_kernel<DT, RINGSIM_MIN, true>, 0));
+  acc(occupancy(tree_flag_kernel<DT, RINGSIM_SUM>, 0));      \
+  acc(occupancy(tree_flag_kernel<DT, RINGSIM_PROD>, 0));     \
+  acc(occupancy(tree_flag_kernel<DT, RINGSIM_MAX>, 0));      \
+  acc(occupancy(tree_flag_kernel<DT, RINGSIM_MIN>, 0));
   RS_TREE_OCC_DT(RINGSIM_INT32)
   RS_TREE_OCC_DT(RINGSIM_INT64)
   RS_TREE_OCC_DT(RINGSIM_FLOAT32)

@@ -8,145 +8,59 @@
 
 namespace ringsim {
 
-// One slice: every line is the fold of the own operand (if any) and the
-// input lines in child order (own first, then first child, then second
-// child), stored to each output FIFO under that FIFO's flag and to the
-// receive buffer. fin[j] / fout[j] (j < nin / nout) point at this step's
-// slots. Arrays are only ever indexed with unrolled constants.
-template <int DT, int OP, bool ONE>
+// One slice of at most one line per thread: every line is the fold of the
+// own operand (if any) and the input lines in child order (own first, then
+// first child, then second child), stored to each output FIFO under that
+// FIFO's flag and to the receive buffer. fin[j] / fout[j] (j < nin / nout)
+// point at this step's slots. Arrays are only ever indexed with unrolled
+// constants.
+template <int DT, int OP>
 __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const char* lp, char* op, int nin,
                                            const uint64_t* const (&fin)[2], const uint32_t (&flag_in)[2],
                                            int nout, uint64_t* const (&fout)[2], const uint32_t (&flag_out)[2],
                                            int vec_ok, bool& stop, const WaitCtx& wc) {
-  if constexpr (ONE) {
-    // At most one line per thread: the shortest path from a flag's arrival
-    // to the next hop's store.
-    const int li = threadIdx.x;
-    if (li >= nlines) return;
-    const int valid = (int)min64(8, nbytes - (int64_t)li * 8);
-    u32x2 x = u32x2{0u, 0u};
-    if (lp) x = load_payload<DT>(lp + (int64_t)li * 8, valid, vec_ok);
-    // Both children's lines are polled together: loads of both go out
-    // before either is checked, and a round re-reads only what is missing.
-    uint64_t v0[2] = {0, 0}, v1[2] = {0, 0};
+  // One line per thread: the shortest path from a flag's arrival to the
+  // next hop's store.
+  const int li = threadIdx.x;
+  if (li >= nlines) return;
+  const int valid = (int)min64(8, nbytes - (int64_t)li * 8);
+  u32x2 x = u32x2{0u, 0u};
+  if (lp) x = load_payload<DT>(lp + (int64_t)li * 8, valid, vec_ok);
+  // Both children's lines are polled together: loads of both go out
+  // before either is checked, and a round re-reads only what is missing.
+  uint64_t v0[2] = {0, 0}, v1[2] = {0, 0};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (j < nin) {
-        v0[j] = ld_relaxed(fin[j] + 2 * li);
-        v1[j] = ld_relaxed(fin[j] + 2 * li + 1);
-      }
+  for (int j = 0; j < 2; ++j) {
+    if (j < nin) {
+      v0[j] = ld_relaxed(fin[j] + 2 * li);
+      v1[j] = ld_relaxed(fin[j] + 2 * li + 1);
     }
-    uint32_t pending = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (j < nin && ((uint32_t)(v0[j] >> 32) != flag_in[j] || (uint32_t)(v1[j] >> 32) != flag_in[j]))
-        pending |= 1u << j;
-    if (pending && !stop) {
-      const uint64_t t0 = wall_clock64();
-      uint32_t spins = 0, verdict = 0;
-      while (pending) {
-        if ((verdict = wait_verdict(wc, t0, ++spins)) != 0u) break;
-        __builtin_amdgcn_s_sleep(1);
-        uint64_t w0[2], w1[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (pending & (1u << j)) {
-            w0[j] = ld_relaxed(fin[j] + 2 * li);
-            w1[j] = ld_relaxed(fin[j] + 2 * li + 1);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if ((pending & (1u << j)) && (uint32_t)(w0[j] >> 32) == flag_in[j] && (uint32_t)(w1[j] >> 32) == flag_in[j]) {
-            v0[j] = w0[j];
-            v1[j] = w1[j];
-            pending &= ~(1u << j);
-          }
-        }
-      }
-      if (verdict) {
-        stop = true;
-        if (verdict != kStopQuiet) raise_error(wc, verdict);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (j < nin) {
-        const u32x2 y = u32x2{(uint32_t)v0[j], (uint32_t)v1[j]};
-        x = (lp || j > 0) ? VOp<DT, OP>::v2(x, y) : y;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (j < nout) {
-        st_relaxed(fout[j] + 2 * li, ((uint64_t)flag_out[j] << 32) | x.x);
-        st_relaxed(fout[j] + 2 * li + 1, ((uint64_t)flag_out[j] << 32) | x.y);
-      }
-    }
-    if (op) store_payload<DT>(op + (int64_t)li * 8, x, valid, vec_ok);
-  } else {
-  // Several lines per thread (lines tid, tid + 256, ...): issue every load
-  // first, then poll again only the lines whose flags are still missing;
-  // every round issues all of its loads before it checks any of them.
-  constexpr int U = kFlagLinesPerThread;
-  u32x2 x[U];
-  uint64_t v0[2][U], v1[2][U];
+  }
   uint32_t pending = 0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int li = threadIdx.x + u * kThreads;
-    x[u] = u32x2{0u, 0u};
-    if (lp && li < nlines) x[u] = load_payload<DT>(lp + (int64_t)li * 8, (int)min64(8, nbytes - (int64_t)li * 8), vec_ok);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int li = threadIdx.x + u * kThreads;
-      v0[j][u] = v1[j][u] = 0;
-      if (j < nin && li < nlines) {
-        v0[j][u] = ld_relaxed(fin[j] + 2 * li);
-        v1[j][u] = ld_relaxed(fin[j] + 2 * li + 1);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (j < nin && threadIdx.x + u * kThreads < nlines &&
-          ((uint32_t)(v0[j][u] >> 32) != flag_in[j] || (uint32_t)(v1[j][u] >> 32) != flag_in[j]))
-        pending |= 1u << (j * U + u);
-    }
-  }
+  for (int j = 0; j < 2; ++j)
+    if (j < nin && ((uint32_t)(v0[j] >> 32) != flag_in[j] || (uint32_t)(v1[j] >> 32) != flag_in[j]))
+      pending |= 1u << j;
   if (pending && !stop) {
     const uint64_t t0 = wall_clock64();
     uint32_t spins = 0, verdict = 0;
     while (pending) {
       if ((verdict = wait_verdict(wc, t0, ++spins)) != 0u) break;
       __builtin_amdgcn_s_sleep(1);
-      uint64_t w0[2][U], w1[2][U];
+      uint64_t w0[2], w1[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (pending & (1u << (j * U + u))) {
-            const int li = threadIdx.x + u * kThreads;
-            w0[j][u] = ld_relaxed(fin[j] + 2 * li);
-            w1[j][u] = ld_relaxed(fin[j] + 2 * li + 1);
-          }
+        if (pending & (1u << j)) {
+          w0[j] = ld_relaxed(fin[j] + 2 * li);
+          w1[j] = ld_relaxed(fin[j] + 2 * li + 1);
         }
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t bit = 1u << (j * U + u);
-          if ((pending & bit) && (uint32_t)(w0[j][u] >> 32) == flag_in[j] && (uint32_t)(w1[j][u] >> 32) == flag_in[j]) {
-            v0[j][u] = w0[j][u];
-            v1[j][u] = w1[j][u];
-            pending &= ~bit;
-          }
+        if ((pending & (1u << j)) && (uint32_t)(w0[j] >> 32) == flag_in[j] && (uint32_t)(w1[j] >> 32) == flag_in[j]) {
+          v0[j] = w0[j];
+          v1[j] = w1[j];
+          pending &= ~(1u << j);
         }
       }
     }
@@ -156,27 +70,20 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
     }
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int li = threadIdx.x + u * kThreads;
-    if (li < nlines) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j < nin) {
-          const u32x2 y = u32x2{(uint32_t)v0[j][u], (uint32_t)v1[j][u]};
-          x[u] = (lp || j > 0) ? VOp<DT, OP>::v2(x[u], y) : y;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j < nout) {
-          st_relaxed(fout[j] + 2 * li, ((uint64_t)flag_out[j] << 32) | x[u].x);
-          st_relaxed(fout[j] + 2 * li + 1, ((uint64_t)flag_out[j] << 32) | x[u].y);
-        }
-      }
-      if (op) store_payload<DT>(op + (int64_t)li * 8, x[u], (int)min64(8, nbytes - (int64_t)li * 8), vec_ok);
+  for (int j = 0; j < 2; ++j) {
+    if (j < nin) {
+      const u32x2 y = u32x2{(uint32_t)v0[j], (uint32_t)v1[j]};
+      x = (lp || j > 0) ? VOp<DT, OP>::v2(x, y) : y;
     }
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j < nout) {
+      st_relaxed(fout[j] + 2 * li, ((uint64_t)flag_out[j] << 32) | x.x);
+      st_relaxed(fout[j] + 2 * li + 1, ((uint64_t)flag_out[j] << 32) | x.y);
+    }
   }
+  if (op) store_payload<DT>(op + (int64_t)li * 8, x, valid, vec_ok);
 }
 
 // One workgroup per (rank, tree, channel, role). Role 0 folds the rank's own
@@ -186,9 +93,7 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
 // it on to the children. Every FIFO carries one step per slice of the
 // channel; its producer owns `tail`, its consumer `head`, and a line's flag
 // is the low 32 bits of (step + 1).
-// ONE: the host has checked that no slice of this launch holds more than one
-// line per thread, so only the one-line path is compiled.
-template <int DT, int OP, bool ONE>
+template <int DT, int OP>
 __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int64_t E = sizeof(T);
@@ -203,7 +108,7 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
   if (role == 1 && root) return;  // the root's up pass starts the broadcast
   const Range cr = tree_channel_range(a.count, t, c, a.nchannels, A);
   if (cr.hi <= cr.lo) return;
-  const int64_t slice = (a.slot_bytes / 2) / E;
+  const int64_t slice = (a.slot_bytes / 2) / E;  // one payload word pair per thread
   const int64_t nsl = div_up(cr.hi - cr.lo, slice);
 
   // FIFOs on each side, in child-slot order; unused entries stay null.
@@ -315,7 +220,7 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
       flag_in[j] = (uint32_t)(in_base[j] + s + 1);
       flag_out[j] = (uint32_t)(out_base[j] + s + 1);
     }
-    tree_lines<DT, OP, ONE>(nlines, nbytes, own ? own + s * slice * E : nullptr, dst ? dst + s * slice * E : nullptr,
+    tree_lines<DT, OP>(nlines, nbytes, own ? own + s * slice * E : nullptr, dst ? dst + s * slice * E : nullptr,
                        nin, fin, flag_in, nout, fout, flag_out, a.vec_ok, stop, wc);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

@@ -81,8 +81,8 @@ def test_tree_matrix(dtype):
 
 
 def test_tree_many_slices_flow_control():
-    """4 MiB per rank over 4 tree channels: 64 slices per channel, eight
-    times the FIFO depth, so every producer waits on its consumer's head."""
+    """4 MiB per rank over 4 tree channels: 256 slices of 2 KiB per channel,
+    32 times the FIFO depth, so every producer waits on its consumer's head."""
     n, count = 8, 1 << 20
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
@@ -180,21 +180,23 @@ def test_tree_degenerate_shapes():
 
 
 @pytest.mark.parametrize("dtype", ["int32", "bfloat16", "int64"])
-def test_tree_kernel_variant_boundary(dtype):
-    """The host runs the tree's one-line-per-thread kernel only when no slice
-    holds more than 256 lines (2 KiB of payload). Tree 0 takes the larger
-    half; halves of exactly 2 KiB and of one 16-byte vector more take
-    different kernels, and both must be whole and bit-exact."""
+def test_tree_channel_and_slice_boundaries(dtype):
+    """A channel carries its share of a tree's half in slices of 2 KiB (one
+    16-byte flag line per thread). Tree 0 takes the larger half; a half of
+    exactly one slice takes one channel and one 16-byte vector more takes
+    two; a half of exactly four slices fills the four channels with one
+    slice each and one vector more gives the first channel a second, short
+    slice. Every case must be whole and bit-exact."""
     e = {"int32": 4, "bfloat16": 2, "int64": 8}[dtype]
-    half = 2048 // e
     n = 8
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
-        for extra in (0, 16 // e):
-            count = 2 * (half + extra)
-            xs = _inputs(n, count, dtype, 1600 + count)
-            G.say(f"tree boundary {dtype} count={count}")
-            got = _run(comm, xs, dtype, "sum")
-            _assert_tree(got, xs, dtype, "sum", f"tree boundary count={count}")
+        for slices in (1, 4):
+            for extra in (0, 16 // e):
+                count = 2 * (slices * 2048 // e + extra)
+                xs = _inputs(n, count, dtype, 1600 + count)
+                G.say(f"tree boundary {dtype} count={count}")
+                got = _run(comm, xs, dtype, "sum")
+                _assert_tree(got, xs, dtype, "sum", f"tree boundary count={count}")
     finally:
         rs.comm_destroy(comm)
