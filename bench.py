@@ -42,7 +42,7 @@ COPY_KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("copy.hip", "ringsim_int
 # exploration and print the same JSON fields.
 WORKLOADS = {
     "ar4x4k": dict(coll="allreduce", nranks=4, count=1024, dtype="float32", nchannels=1,
-                   chunk_bytes=524_288, synth_workload=1, op="sum", proto="bulk",
+                   chunk_bytes=524_288, synth_workload=1, op="sum", proto="bulk", graph_calls=100,
                    desc="ring all-reduce sum, 4 simulated ranks x 1024 fp32 (integers in [-8, 8]), 1 channel, "
                         "bulk protocol (latency-bound: report us per call)"),
     "ar8x64": dict(coll="allreduce", nranks=8, count=16_777_216, dtype="float32", nchannels=8,
@@ -359,6 +359,33 @@ def size_sweep(args) -> int:
     return 0
 
 
+def graph_timing(call, calls: int, stream, launches: int = 20) -> dict:
+    """Captures `calls` back-to-back calls into one HIP graph (torch.cuda.CUDAGraph)
+    and times `launches` launches of it with one HIP event pair each, on the
+    launch stream: microseconds per call with no host work between calls."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            call()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    torch.cuda._sleep(2_000_000)
+    for a, b in zip(starts, ends):
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 / calls for a, b in zip(starts, ends))
+    return {"calls": calls, "launches": launches, "us_per_call": round(statistics.median(per), 3),
+            "us_per_call_min": round(per[0], 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +411,9 @@ def main() -> int:
     ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag", "wide"])
     ap.add_argument("--algo", default="auto", choices=["auto", "ring", "tree"],
                     help="all-reduce algorithm for --sweep (auto: the library's choice)")
+    ap.add_argument("--graph-calls", type=int, default=-1,
+                    help="also time K back-to-back calls captured in one HIP graph (0 = off; default: the "
+                         "workload's own setting, 100 calls for ar4x4k, else off)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time the library's copy kernel on 1 GiB (a one-rank all-to-all) instead; used to "
                          "scale the HBM byte counters")
@@ -537,6 +567,24 @@ def main() -> int:
         f"compulsory rate {compulsory / t_avg / 1e9:.0f} GB/s  D2D copy {d2d:.0f} GB/s "
         f"(cache-resident {cache_copy:.0f} GB/s" + (f", this byte mix {mixed:.0f} GB/s)" if mixed else ")"))
 
+    graph = None
+    gk = args.graph_calls if args.graph_calls >= 0 else w.get("graph_calls", 0)
+    if gk > 0:
+        graph = graph_timing(call, gk, stream)
+        if check is not None:
+            ok = True
+            for r in range(n):
+                got = recv[r].view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" else recv[r].cpu().numpy()
+                ok &= bool(np.array_equal(got.view(np.uint8), np.asarray(want[r]).view(np.uint8)))
+            graph["parity"] = "bit-exact vs oracle" if ok else "MISMATCH vs oracle"
+            if not ok:
+                log("[bench] graph launches: MISMATCH vs oracle")
+                return 1
+        if rs.get_async_error(comm) != rs.SUCCESS:
+            log("[bench] graph launches left the communicator in error state")
+            return 1
+        log(f"[bench] graph of {gk} calls: {graph['us_per_call']:.2f} us per call")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
@@ -595,6 +643,7 @@ def main() -> int:
             "mixed_copy_gbs": round(mixed, 1) if mixed else None,
             "parity": check,
             "kernel_source_hash": src_hash,
+            "graph": graph,
         },
     }
     rs.comm_destroy(comm)

@@ -27,6 +27,15 @@
  *     ProcessGroupNCCL、Stream、Event 与 Work"). Calls on one communicator must
  *     be issued from one host thread and must be ordered on the device (one
  *     stream, or streams ordered by events): the FIFOs are shared state.
+ *   - Calls may be captured into a HIP graph (stream capture): a call
+ *     enqueues kernel launches only (no memset, copy, event or
+ *     synchronization), and every kernel reads where its FIFOs stand from
+ *     the communicator's persistent step counters when it starts, so graph
+ *     launches and direct calls may follow one another in any order as long
+ *     as they are ordered on the device. What ringsim_comm_query reports
+ *     about the latest call describes the capture, not the launches. A graph
+ *     holding a communicator's calls must not be launched after
+ *     ringsim_comm_destroy.
  *   - count == 0 is a successful no-op; nranks == 1 is a local copy
  *     ("NCCL" book, enqueue chapter, taskAppend).
  *   - Every kernel polls an abort word and bounds each wait by a timeout; a
@@ -203,8 +212,10 @@ ringsim_result_t ringsim_comm_init(ringsim_comm_t* comm, int nranks, int nchanne
 ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int nchannels, int proto,
                                           const ringsim_config_t* cfg);
 
-/* Waits for the communicator's last stream, frees its device memory and
- * invalidates the handle. */
+/* Waits for all work on the device (hipDeviceSynchronize: the streams the
+ * communicator was used on may no longer exist), frees its device memory
+ * and invalidates the handle. Not to be called while a stream that holds
+ * its calls is being captured. */
 ringsim_result_t ringsim_comm_destroy(ringsim_comm_t comm);
 
 ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* info);
@@ -238,8 +249,11 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
                                   size_t count, int dtype, ringsim_stream_t stream);
 
 /* Reports the communicator's asynchronous state: RINGSIM_SUCCESS,
- * RINGSIM_IN_PROGRESS while enqueued work is still running and no error is
- * known, or the error a kernel or ringsim_abort left behind. */
+ * RINGSIM_IN_PROGRESS while enqueued work on the stream of the latest call
+ * is still running and no error is known, or the error a kernel or
+ * ringsim_abort left behind. While that stream is being captured into a
+ * graph it is not queried (that would end the capture): only known errors
+ * are reported. */
 ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error);
 
 /* Raises the abort word that every spinning kernel polls; running kernels

@@ -681,9 +681,11 @@ ringsim_result_t ringsim_comm_destroy(ringsim_comm_t comm) {
     std::lock_guard<std::mutex> lk(g_live_mu);
     g_live.erase(comm);
   }
-  // Every kernel bounds its waits, so this returns even after an abort.
-  hipError_t e = comm->has_last_stream ? hipStreamSynchronize(comm->last_stream) : hipSuccess;
-  if (e != hipSuccess) e = hipDeviceSynchronize();
+  // Every kernel bounds its waits, so this returns even after an abort. The
+  // whole device is synchronized rather than the last stream the
+  // communicator saw: that stream may have been destroyed since (freeing
+  // device memory waits for the device anyway).
+  const hipError_t e = hipDeviceSynchronize();
   free_comm_memory(comm);
   comm->start_magic = kDeadMagic;
   comm->end_magic = kDeadMagic;
@@ -773,7 +775,15 @@ ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* 
   if (res != RINGSIM_SUCCESS) return res;
   if (!async_error) return RINGSIM_INVALID_ARGUMENT;
   ringsim_result_t st = poll_async(comm);
-  if (st == RINGSIM_SUCCESS && comm->has_last_stream) {
+  // A stream that is being captured into a graph must not be queried (that
+  // would end the capture); its calls have not run yet, and only the error
+  // words are reported.
+  bool query = comm->has_last_stream;
+  if (query) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    query = hipStreamIsCapturing(comm->last_stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone;
+  }
+  if (st == RINGSIM_SUCCESS && query) {
     const hipError_t q = hipStreamQuery(comm->last_stream);
     if (q == hipErrorNotReady) {
       st = RINGSIM_IN_PROGRESS;
