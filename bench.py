@@ -567,6 +567,30 @@ def main() -> int:
         f"compulsory rate {compulsory / t_avg / 1e9:.0f} GB/s  D2D copy {d2d:.0f} GB/s "
         f"(cache-resident {cache_copy:.0f} GB/s" + (f", this byte mix {mixed:.0f} GB/s)" if mixed else ")"))
 
+    # Back-to-back buckets: one event pair around all of them (no host
+    # synchronization in between), three times from bucket 0.
+    back_to_back = None
+    if coll == "allreduce" and nbuckets > 1:
+        runs = []
+        for _ in range(3):
+            bucket[0] = 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(2_000_000)
+            a.record(stream)
+            for _ in range(nbuckets):
+                call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            runs.append(a.elapsed_time(b) * 1e3 / nbuckets)
+        if rs.get_async_error(comm) != rs.SUCCESS:
+            log("[bench] back-to-back buckets left the communicator in error state")
+            return 1
+        back_to_back = {"calls": nbuckets, "us_per_call": round(statistics.median(runs), 2),
+                        "busbw_gbs": round(per_rank_bytes / (statistics.median(runs) * 1e-6) / 1e9
+                                           * bus_factor(coll, n), 2)}
+        log(f"[bench] {nbuckets} buckets back to back: {back_to_back['us_per_call']:.1f} us per bucket")
+
     graph = None
     gk = args.graph_calls if args.graph_calls >= 0 else w.get("graph_calls", 0)
     if gk > 0:
@@ -644,6 +668,7 @@ def main() -> int:
             "parity": check,
             "kernel_source_hash": src_hash,
             "graph": graph,
+            "back_to_back": back_to_back,
         },
     }
     rs.comm_destroy(comm)

@@ -188,6 +188,7 @@ typedef struct {
   int last_algo;               /* algorithm of the latest all-reduce: RINGSIM_ALGO_RING/TREE, 0 if none */
   int line_max_workgroups_per_channel; /* most workgroups per channel a FLAG/WIDE launch may take */
   int last_workgroups_per_channel;     /* workgroups per channel of the latest ring call, 0 if none */
+  int last_tree_channels;              /* channels per tree of the latest all-reduce, 0 if it ran the ring */
 } ringsim_comm_info_t;
 
 /* Fills *cfg with the defaults. Environment overrides, read by this call:

@@ -97,6 +97,7 @@ class CommInfo(ctypes.Structure):
         ("last_algo", ctypes.c_int),
         ("line_max_workgroups_per_channel", ctypes.c_int),
         ("last_workgroups_per_channel", ctypes.c_int),
+        ("last_tree_channels", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:

@@ -107,6 +107,7 @@ struct ringsim_comm {
   uint64_t calls;
   int last_proto;
   int last_wpc;
+  int last_tree_channels;  // channels per tree of the latest all-reduce, 0 = ring
   int algo;                // configured all-reduce algorithm
   int last_algo;
   int tree_channels;       // channels per tree in the tree FIFO arrays
@@ -396,6 +397,7 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   a.count = (int64_t)count;
   a.nranks = c->nranks;
   a.nchannels = tree_channels_for(c, count * (size_t)dtype_size(dtype));
+  c->last_tree_channels = a.nchannels;
   a.ch_stride = c->tree_channels;
   a.nslots = kTreeSlots;
   a.slot_bytes = kTreeSlotBytes;
@@ -442,6 +444,7 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
     const bool tree = c->algo == RINGSIM_ALGO_TREE ||
                       (c->algo == RINGSIM_ALGO_AUTO && auto_picks_tree(c, dtype, op, count));
     c->last_algo = tree ? RINGSIM_ALGO_TREE : RINGSIM_ALGO_RING;
+    c->last_tree_channels = 0;
     if (tree) return launch_tree(c, sb, rb, count, dtype, op, vec, s);
   }
   RingArgs a;
@@ -719,6 +722,7 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
   info->last_algo = comm->last_algo;
   info->line_max_workgroups_per_channel = comm->line_wpc_max;
   info->last_workgroups_per_channel = comm->last_wpc;
+  info->last_tree_channels = comm->last_tree_channels;
   return RINGSIM_SUCCESS;
 }
 

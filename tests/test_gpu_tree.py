@@ -191,12 +191,13 @@ def test_tree_channel_and_slice_boundaries(dtype):
     n = 8
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
-        for slices in (1, 4):
-            for extra in (0, 16 // e):
+        for slices, channels in ((1, (1, 2)), (4, (4, 4))):
+            for extra, want_channels in zip((0, 16 // e), channels):
                 count = 2 * (slices * 2048 // e + extra)
                 xs = _inputs(n, count, dtype, 1600 + count)
                 G.say(f"tree boundary {dtype} count={count}")
                 got = _run(comm, xs, dtype, "sum")
+                assert rs.comm_query(comm)["last_tree_channels"] == want_channels
                 _assert_tree(got, xs, dtype, "sum", f"tree boundary count={count}")
     finally:
         rs.comm_destroy(comm)
