@@ -5,8 +5,9 @@
 // Call path ("NCCL" book, enqueue chapter: ncclEnqueueCheck -> taskAppend ->
 // plan -> launch, collapsed): check the handle and its magic words, check the
 // arguments, return early for count == 0, copy locally for one rank, choose
-// the protocol by size, fill one kernel-argument block and enqueue one kernel
-// on the caller's stream. Nothing waits for the device.
+// the algorithm, protocol and workgroups per channel with the cost model
+// (ring_model.h), fill one kernel-argument block and enqueue one kernel on
+// the caller's stream. Nothing waits for the device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
