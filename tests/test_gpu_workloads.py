@@ -87,20 +87,27 @@ def test_workload3_ddp_buckets_back_to_back():
         rs.comm_destroy(comm)
 
 
+@pytest.mark.parametrize("choice", ["threshold", "auto"])
 @pytest.mark.parametrize("op", ["sum", "max"])
-def test_workload4_size_sweep(op):
-    """16 ranks, int32 in [-2^20, 2^20], 8 B .. 256 MiB per rank; flag-packed
-    below 64 KiB, bulk above (the sweep's own fixed threshold, not the cost
-    model), 16 channels, ring algorithm."""
+def test_workload4_size_sweep(op, choice):
+    """16 ranks, int32 in [-2^20, 2^20], 8 B .. 256 MiB per rank, 16 channels.
+    "threshold": the ring, flag-packed below 64 KiB and bulk above (the
+    sweep's own fixed threshold); "auto": whatever algorithm, protocol and
+    workgroups the cost model takes (the tree, FLAG, WIDE or BULK). Integer
+    sums and maxima do not depend on the fold order, so both equal the ring
+    oracle."""
     import torch
 
     n, nch = 16, 16
-    comm = rs.comm_init(n, nch, "auto", flag_threshold_bytes=65536, algo="ring")
+    if choice == "threshold":
+        comm = rs.comm_init(n, nch, "auto", flag_threshold_bytes=65536, algo="ring")
+    else:
+        comm = rs.comm_init(n, nch, "auto")
     try:
         for k, size in enumerate(synth.WORKLOADS[4]["sizes_bytes"]):
             count = size // 4
             want_proto = 2 if size < 65536 else 1
-            G.say(f"sweep op={op} bytes/rank={size} proto={'flag' if want_proto == 2 else 'bulk'}")
+            G.say(f"sweep {choice} op={op} bytes/rank={size}")
             if size <= (4 << 20):
                 xs = synth.rank_inputs(4, n, count, "int32", "int", lo=-(1 << 20), hi=1 << 20, bucket=k)
                 send = [G.to_device(x, "int32") for x in xs]
@@ -111,7 +118,8 @@ def test_workload4_size_sweep(op):
             rs.allreduce(comm, send, recv, op=op)
             G.sync()
             G.check_comm_ok(comm)
-            assert rs.comm_query(comm)["last_proto"] == want_proto, f"size {size}"
+            if choice == "threshold":
+                assert rs.comm_query(comm)["last_proto"] == want_proto, f"size {size}"
             assert _all_ranks_equal(recv), f"size {size}: ranks disagree"
             if xs is not None:
                 want = oracle.ring_allreduce(xs, op, "int32", nchannels=nch)
