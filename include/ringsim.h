@@ -160,8 +160,8 @@ typedef struct {
   int algo;                    /* ringsim_algo_t for all-reduces; default AUTO, env RINGSIM_ALGO=ring|tree|auto */
   int line_workgroups_per_channel; /* FLAG/WIDE: most workgroups per (rank, channel) of a launch: 1, 2, 4
                                       or 8 (fewer where the device cannot hold them all); default 0 = per
-                                      call, the fewest that make every step of a workgroup at most 128
-                                      lines; env RINGSIM_LINE_WPC */
+                                      call, the count the cost model predicts fastest with at most two
+                                      workgroups per compute unit; env RINGSIM_LINE_WPC */
 } ringsim_config_t;
 
 /* Read-only description of a communicator. */

@@ -52,6 +52,10 @@ OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 PROTOS = {"auto": 0, "bulk": 1, "flag": 2, "wide": 3}
 ALGOS = {"auto": 0, "ring": 1, "tree": 2}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "alltoall": 3}
+# Limits of the ABI (the RINGSIM_MAX_* macros of the header).
+MAX_RANKS = 64
+MAX_CHANNELS = 64
+MAX_WORKGROUPS_PER_CHANNEL = 16
 
 
 class RingsimError(RuntimeError):

@@ -33,6 +33,36 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, f)
 
 
+def _header_struct_fields(name):
+    import re
+
+    with open(rs.HEADER_PATH) as f:
+        text = f.read()
+    body = re.search(r"typedef struct \{((?:(?!typedef struct).)*?)\}\s*" + name + ";", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return [(m.group(1), m.group(2)) for m in re.finditer(r"^\s*([a-z_0-9]+)\s+([a-z_0-9]+);", body, re.M)]
+
+
+def test_binding_mirrors_the_header():
+    """The ctypes structures list the header's fields in order, with C types
+    of the same size, and the binding's limits equal the header's macros."""
+    import re
+
+    sizes = {"int": ctypes.sizeof(ctypes.c_int), "size_t": ctypes.sizeof(ctypes.c_size_t),
+             "uint64_t": 8, "double": 8}
+    for cname, pycls in (("ringsim_config_t", rs.Config), ("ringsim_comm_info_t", rs.CommInfo)):
+        fields = _header_struct_fields(cname)
+        assert [f for _, f in fields] == [f for f, _ in pycls._fields_], cname
+        for (ctype, f), (_, pytype) in zip(fields, pycls._fields_):
+            assert sizes[ctype] == ctypes.sizeof(pytype), (cname, f)
+    with open(rs.HEADER_PATH) as f:
+        text = f.read()
+    macros = dict(re.findall(r"#define RINGSIM_(MAX_[A-Z_]+) (\d+)", text))
+    assert int(macros["MAX_RANKS"]) == rs.MAX_RANKS
+    assert int(macros["MAX_CHANNELS"]) == rs.MAX_CHANNELS
+    assert int(macros["MAX_WORKGROUPS_PER_CHANNEL"]) == rs.MAX_WORKGROUPS_PER_CHANNEL
+
+
 def test_error_strings(L):
     for code in (0, 1, 2, 3, 4, 5, 7, 8):
         assert rs.error_string(code)

@@ -187,6 +187,18 @@ def test_degenerate_shapes():
         rs.comm_destroy(comm)
 
 
+@pytest.mark.parametrize("proto", ["bulk", "flag", "wide"])
+def test_maximum_ranks_and_channels(proto):
+    """The limits of the ABI: RINGSIM_MAX_RANKS (64) ranks over 4 channels,
+    and RINGSIM_MAX_CHANNELS (64) channels over 4 ranks, with ragged counts
+    that span several loops per channel."""
+    for n, nch, count in ((rs.MAX_RANKS, 4, 64 * 4 * 300 + 37), (4, rs.MAX_CHANNELS, 64 * 4 * 300 + 5)):
+        xs = _inputs(n, count, "float32", 900 + n)
+        got = _run_allreduce(xs, "float32", "sum", nch, proto, chunk_bytes=1024)
+        want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=nch, chunk_bytes=1024)
+        _assert_same(got, want, "float32", f"limits N={n} C={nch} proto={proto}")
+
+
 def test_back_to_back_calls_one_stream():
     # many collectives of different shapes and both protocols on one stream:
     # the FIFO counters carry over from call to call

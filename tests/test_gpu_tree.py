@@ -80,6 +80,24 @@ def test_tree_matrix(dtype):
             rs.comm_destroy(comm)
 
 
+@pytest.mark.parametrize("dtype", ["float32", "int32"])
+def test_tree_maximum_ranks(dtype):
+    """RINGSIM_MAX_RANKS (64) ranks: trees of depth 6 in which every rank is
+    a leaf of exactly one of the two trees, one tree channel per call (64
+    ranks x 4 workgroups already fill the device)."""
+    n = rs.MAX_RANKS
+    comm = rs.comm_init(n, 4, "auto", algo="tree")
+    try:
+        for count in (1, 1027, 40_003):
+            xs = _inputs(n, count, dtype, 3000 + count)
+            G.say(f"tree N={n} count={count} dtype={dtype}")
+            got = _run(comm, xs, dtype, "sum")
+            assert rs.comm_query(comm)["last_algo"] == 2
+            _assert_tree(got, xs, dtype, "sum", f"N={n} count={count}")
+    finally:
+        rs.comm_destroy(comm)
+
+
 def test_tree_many_slices_flow_control():
     """4 MiB per rank over 4 tree channels: 256 slices of 2 KiB per channel,
     32 times the FIFO depth, so every producer waits on its consumer's head."""
