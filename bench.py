@@ -349,11 +349,13 @@ def size_sweep(args) -> int:
         t = statistics.median([a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends)])
         info = rs.comm_query(comm)
         algo = {1: "ring", 2: "tree"}.get(info["last_algo"], "?") if coll == "allreduce" else "ring"
-        proto = "flag" if algo == "tree" else {1: "bulk", 2: "flag", 3: "wide"}.get(info["last_proto"], "?")
+        proto = "wide" if algo == "tree" else {1: "bulk", 2: "flag", 3: "wide"}.get(info["last_proto"], "?")
         busbw = size / t * bus_factor(coll, n) / 1e9
         byts = algorithmic_bytes(coll, n, size)
         print(json.dumps({"coll": coll, "nranks": n, "nchannels": nch, "op": args.sweep_op, "bytes_per_rank": size,
-                          "algo": algo, "proto": proto, "wpc": info["last_workgroups_per_channel"],
+                          "algo": algo, "proto": proto,
+                          "wpc": 0 if algo == "tree" else info["last_workgroups_per_channel"],
+                          "tree_channels": info["last_tree_channels"],
                           "us": round(t * 1e6, 2), "busbw_gbs": round(busbw, 3),
                           "alg_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4), "sampled_parity": ok}), flush=True)
         if not ok:

@@ -127,15 +127,17 @@ typedef enum {
  * reducing one half of the buffer up to its root and broadcasting the result
  * back down. Tree 1 takes elements [h, count) with
  * h = min(count, alignUp(ceil(count/2), 16/elemsize)); a rank folds its own
- * data, then its first child's partial, then its second child's. Each half
- * is split over channels of one 2 KiB slice (one 16-byte flag line per
- * thread) each, as many as allow one tree workgroup per compute unit
- * (4 x N x channels <= CUs); longer channels pipeline slice by slice. The tree
- * always moves flag-packed lines and needs 2*log2(N) dependent hops instead
- * of the ring's 2(N-1). AUTO takes the tree only where the fold order cannot
- * change a result bit (integer types, and max/min of any type) and the cost
- * model predicts it faster; with proto = BULK it always takes the ring. The
- * algorithm applies to ringsim_allreduce only. */
+ * data, then its first child's partial, then its second child's. The tree
+ * moves WIDE lines (12 payload bytes and the flag in one 16-byte line, 8
+ * payload bytes for int64), one line per thread and FIFO step, so a step
+ * carries 3 KiB (2 KiB for int64). Each half is split over channels of one
+ * step each, as many as allow one tree workgroup per compute unit
+ * (4 x N x channels <= CUs); longer channels pipeline step by step. The tree
+ * needs 2*log2(N) dependent hops instead of the ring's 2(N-1). AUTO takes
+ * the tree only where the fold order cannot change a result bit (integer
+ * types, and max/min of any type) and the cost model predicts it faster;
+ * with proto = BULK it always takes the ring. The algorithm applies to
+ * ringsim_allreduce only. */
 typedef enum {
   RINGSIM_ALGO_AUTO = 0,
   RINGSIM_ALGO_RING = 1,
@@ -284,10 +286,10 @@ ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t
 ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
 
 /* Host-only cost model of the tree all-reduce with `tree_channels` channels
- * per tree and `bytes_per_rank` bytes per rank on a 256-CU device: base +
- * 2 x tree depth x the per-hop latency of one slice (one 16-byte flag line
- * per thread) + the load of the tree's workgroups on the compute units + one
- * further step per further slice of a channel. Writes the predicted
+ * per tree and `bytes_per_rank` bytes per rank of a 4-byte type on a 256-CU
+ * device: base + 2 x tree depth x the per-hop latency of one step (one WIDE
+ * line per thread) + the load of the tree's workgroups on the compute units
+ * + one further step per further 3 KiB of a channel. Writes the predicted
  * microseconds. */
 ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us);
 

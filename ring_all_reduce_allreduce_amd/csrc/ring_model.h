@@ -56,13 +56,12 @@ struct RingModel {
   double line_step_us[2][2] = {{0.971, 0.097}, {0.888, 0.095}};
   double line_crowd = 0.368;
   double line_gbs = 4540.0;
-  // Double-binary tree (flag lines, one line per thread per step): base,
-  // per hop a + b * lines / 256, per compute-unit load of its workgroups,
-  // and per further step (scaled by that load once it passes one).
-  double tree_base_us = 6.03;
-  double tree_hop_us[2] = {0.828, 0.118};
-  double tree_crowd_us = 2.35;
-  double tree_step_us = 1.636;
+  // Double-binary tree (WIDE lines, one line per thread per step): base,
+  // per hop a + b * lines / 256, and per further step (scaled by the load of
+  // its workgroups on the compute units once that passes one).
+  double tree_base_us = 6.73;
+  double tree_hop_us[2] = {0.833, 0.018};
+  double tree_step_us = 1.127;
 };
 
 enum ModelColl : int { kModelAllReduce = 0, kModelReduceScatter = 1, kModelAllGather = 2 };
@@ -123,20 +122,20 @@ inline double line_model_us(const RingModel& m, int coll, int nranks, int nchann
 
 // Predicted microseconds of a double-binary-tree all-reduce: the reduce
 // climbs `depth` hops to each root and the broadcast descends as many, one
-// slice of `slice_bytes` per step in flag-packed lines; each tree's half of
-// the buffer is split over `tree_channels` channels, and the 4 x N x
-// tree_channels workgroups (two trees, an up and a down role each) share
-// `cus` compute units. Fitted to the tree's own sweeps at 16 and 8 ranks
-// (within 8% from 1 KiB to 512 KiB per rank).
+// slice of `slice_bytes` per step in lines of `line_payload` bytes; each
+// tree's half of the buffer is split over `tree_channels` channels, and the
+// 4 x N x tree_channels workgroups (two trees, an up and a down role each)
+// share `cus` compute units. Fitted to the tree's own sweeps at 16, 8 and 4
+// ranks, sum and max, 1 KiB to 1 MiB per rank (within 6%).
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double slice_bytes,
-                            double bytes_per_rank, int cus) {
+                            double line_payload, double bytes_per_rank, int cus) {
   if (nranks <= 1) return m.base_us;
   const double per_channel = std::ceil(bytes_per_rank / 2.0 / tree_channels);
-  const double lines = std::ceil(std::min(per_channel, slice_bytes) / 8.0);
+  const double lines = std::ceil(std::min(per_channel, slice_bytes) / line_payload);
   const double steps = std::max(1.0, std::ceil(per_channel / slice_bytes));
   const double load = 4.0 * nranks * tree_channels / cus;
   return m.tree_base_us + 2.0 * depth * (m.tree_hop_us[0] + m.tree_hop_us[1] * lines / 256.0) +
-         m.tree_crowd_us * load + (steps - 1.0) * m.tree_step_us * std::max(1.0, load);
+         (steps - 1.0) * m.tree_step_us * std::max(1.0, load);
 }
 
 }  // namespace ringsim

@@ -358,33 +358,37 @@ ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void*
   return RINGSIM_SUCCESS;
 }
 
-// Tree channels of one all-reduce: one slice (one line per thread) of the
-// half buffer its tree owns per channel, and at most one tree workgroup per
-// compute unit: with more, the steps of the workgroups that share a unit
-// queue behind each other and a longer pipeline per channel is faster.
-constexpr int64_t kTreeSliceBytes = kTreeSlotBytes / 2;
+// Payload bytes of one tree step (one WIDE line per thread: 12 bytes, 8 for
+// int64).
+int64_t tree_slice_bytes(int esize) { return (int64_t)kThreads * (esize == 8 ? 8 : 12); }
 
-int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank) {
-  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), kTreeSliceBytes);
+// Tree channels of one all-reduce: one slice of the half buffer its tree owns
+// per channel, and at most one tree workgroup per compute unit: with more,
+// the steps of the workgroups that share a unit queue behind each other and
+// a longer pipeline per channel is faster.
+int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank, int esize) {
+  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), tree_slice_bytes(esize));
   const int64_t per_cu_cap = std::max<int64_t>(1, c->compute_units / (4 * (int64_t)c->nranks));
   return (int)std::max<int64_t>(1, std::min<int64_t>({want, per_cu_cap, (int64_t)c->tree_channels}));
 }
 
-double tree_predict_us(const ringsim_comm* c, size_t bytes_per_rank) {
+double tree_predict_us(const ringsim_comm* c, size_t bytes_per_rank, int esize) {
   const RingModel m;
-  return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank), (double)kTreeSliceBytes,
-                       (double)bytes_per_rank, c->compute_units);
+  const int64_t slice = tree_slice_bytes(esize);
+  return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank, esize), (double)slice,
+                       (double)(slice / kThreads), (double)bytes_per_rank, c->compute_units);
 }
 
 // AUTO's algorithm: the tree only where the fold order cannot show in the
 // result (integers wrap associatively; max/min pick one input), only when
-// the flag-packed lines it moves are allowed (protocol AUTO or FLAG), and
+// the flag-packed lines it moves are allowed (any protocol but BULK), and
 // only when it is predicted to be faster than the ring.
 bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t count) {
   const bool order_free = dtype == RINGSIM_INT32 || dtype == RINGSIM_INT64 || op == RINGSIM_MAX || op == RINGSIM_MIN;
-  const bool lines_ok = c->proto == RINGSIM_PROTO_AUTO || c->proto == RINGSIM_PROTO_FLAG;
+  const bool lines_ok = c->proto != RINGSIM_PROTO_BULK;
   if (!order_free || !lines_ok || c->tree_channels < 1) return false;
-  return tree_predict_us(c, count * (size_t)dtype_size(dtype)) < pick_proto(c, kAllReduce, count, dtype).us;
+  return tree_predict_us(c, count * (size_t)dtype_size(dtype), dtype_size(dtype)) <
+         pick_proto(c, kAllReduce, count, dtype).us;
 }
 
 ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const* rb, size_t count, int dtype,
@@ -397,7 +401,7 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   }
   a.count = (int64_t)count;
   a.nranks = c->nranks;
-  a.nchannels = tree_channels_for(c, count * (size_t)dtype_size(dtype));
+  a.nchannels = tree_channels_for(c, count * (size_t)dtype_size(dtype), dtype_size(dtype));
   c->last_tree_channels = a.nchannels;
   a.ch_stride = c->tree_channels;
   a.nslots = kTreeSlots;
@@ -865,8 +869,9 @@ ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t 
   if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || tree_channels < 1 || tree_channels > RINGSIM_MAX_CHANNELS || !us)
     return RINGSIM_INVALID_ARGUMENT;
   const RingModel m;
-  // A 256-CU device, as the ring model above.
-  *us = tree_model_us(m, nranks, double_tree_depth(nranks), tree_channels, (double)kTreeSliceBytes,
+  // A 256-CU device, as the ring model above; 4-byte elements.
+  const int64_t slice = tree_slice_bytes(4);
+  *us = tree_model_us(m, nranks, double_tree_depth(nranks), tree_channels, (double)slice, (double)(slice / kThreads),
                       (double)bytes_per_rank, 256);
   return RINGSIM_SUCCESS;
 }

@@ -87,7 +87,7 @@ struct TreeArgs {
   int nchannels;        // tree channels of this launch (<= ch_stride)
   int ch_stride;        // tree channels in the FIFO and counter arrays
   int nslots;
-  int slot_bytes;       // kTreeSlotBytes: one flag line per thread, half of it payload
+  int slot_bytes;       // kTreeSlotBytes: one WIDE line per thread
   int head_every;       // consumers publish `head` every this many steps
   int vec_ok;
   int skip_rank;
@@ -101,9 +101,9 @@ struct TreeArgs {
 };
 
 constexpr int kTreeSlots = 8;
-// One 16-byte line per thread: every step of a tree workgroup is a single
-// load, fold and store per thread, the shortest path from a child's flag to
-// the parent's store.
+// One 16-byte WIDE line per thread: every step of a tree workgroup is a
+// single load, fold and store per thread, the shortest path from a child's
+// flag to the parent's store.
 constexpr int kTreeSlotBytes = kThreads * 16;
 
 struct CopyArgs {
@@ -124,7 +124,7 @@ hipError_t launch_ring_lines_half(const RingArgs& a, int line_proto, int mode, i
 hipError_t launch_ring_lines_one(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_ring_lines_multi(const RingArgs& a, int line_proto, int mode, int dtype, int op, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
-// Double-binary tree: one slot (one line per thread) per step.
+// Double-binary tree: one slot (one WIDE line per thread) per step.
 hipError_t launch_tree_kernel(const TreeArgs& a, int dtype, int op, hipStream_t s);
 // Max co-resident workgroups per CU over every instantiation of a kernel
 // family (the bulk kernels launched with `lds_bytes` of dynamic LDS).

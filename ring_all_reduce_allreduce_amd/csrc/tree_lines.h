@@ -1,9 +1,11 @@
-// tree_flag.h -- double-binary-tree all-reduce over flag-packed lines
+// tree_lines.h -- double-binary-tree all-reduce over flag-packed lines
 // ("NCCL" book, ch. 4: two binary trees, each reducing one half of the
-// buffer up to its root and broadcasting it back down).
+// buffer up to its root and broadcasting it back down). Every FIFO step is
+// one WIDE line per thread (line_format.h: 12 payload bytes and the flag in
+// one 128-bit device-coherent access, 8 payload bytes for int64).
 #pragma once
 
-#include "ringsim_device.h"
+#include "line_format.h"
 #include "tree_plan.h"
 
 namespace ringsim {
@@ -12,54 +14,47 @@ namespace ringsim {
 // own operand (if any) and the input lines in child order (own first, then
 // first child, then second child), stored to each output FIFO under that
 // FIFO's flag and to the receive buffer. fin[j] / fout[j] (j < nin / nout)
-// point at this step's slots. Arrays are only ever indexed with unrolled
+// are this step's slots. Arrays are only ever indexed with unrolled
 // constants.
 template <int DT, int OP>
 __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const char* lp, char* op, int nin,
-                                           const uint64_t* const (&fin)[2], const uint32_t (&flag_in)[2],
-                                           int nout, uint64_t* const (&fout)[2], const uint32_t (&flag_out)[2],
-                                           int vec_ok, bool& stop, const WaitCtx& wc) {
+                                           const Slot<kLineWide> (&fin)[2], const uint32_t (&flag_in)[2],
+                                           int nout, const Slot<kLineWide> (&fout)[2],
+                                           const uint32_t (&flag_out)[2], int vec_ok, bool& stop,
+                                           const WaitCtx& wc) {
+  using F = LineFmt<kLineWide, DT>;
   // One line per thread: the shortest path from a flag's arrival to the
   // next hop's store.
   const int li = threadIdx.x;
   if (li >= nlines) return;
-  const int valid = (int)min64(8, nbytes - (int64_t)li * 8);
-  u32x2 x = u32x2{0u, 0u};
-  if (lp) x = load_payload<DT>(lp + (int64_t)li * 8, valid, vec_ok);
+  const int valid = (int)min64(F::PB, nbytes - (int64_t)li * F::PB);
+  u32x4 x = u32x4{0u, 0u, 0u, 0u};
+  if (lp) x = load_user<DT, F::PD>(lp + (int64_t)li * F::PB, valid, vec_ok);
   // Both children's lines are polled together: loads of both go out
   // before either is checked, and a round re-reads only what is missing.
-  uint64_t v0[2] = {0, 0}, v1[2] = {0, 0};
+  u32x4 v[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j < nin) {
-      v0[j] = ld_relaxed(fin[j] + 2 * li);
-      v1[j] = ld_relaxed(fin[j] + 2 * li + 1);
-    }
-  }
+  for (int j = 0; j < 2; ++j)
+    if (j < nin) v[j] = fin[j].load(li);
   uint32_t pending = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < nin && ((uint32_t)(v0[j] >> 32) != flag_in[j] || (uint32_t)(v1[j] >> 32) != flag_in[j]))
-      pending |= 1u << j;
+    if (j < nin && !Slot<kLineWide>::ready(v[j], flag_in[j])) pending |= 1u << j;
   if (pending && !stop) {
     const uint64_t t0 = wall_clock64();
     uint32_t spins = 0, verdict = 0;
     while (pending) {
       if ((verdict = wait_verdict(wc, t0, ++spins)) != 0u) break;
       __builtin_amdgcn_s_sleep(1);
-      uint64_t w0[2], w1[2];
+      compiler_fence();
+      u32x4 w[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (pending & (1u << j)) w[j] = fin[j].load(li);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        if (pending & (1u << j)) {
-          w0[j] = ld_relaxed(fin[j] + 2 * li);
-          w1[j] = ld_relaxed(fin[j] + 2 * li + 1);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if ((pending & (1u << j)) && (uint32_t)(w0[j] >> 32) == flag_in[j] && (uint32_t)(w1[j] >> 32) == flag_in[j]) {
-          v0[j] = w0[j];
-          v1[j] = w1[j];
+        if ((pending & (1u << j)) && Slot<kLineWide>::ready(w[j], flag_in[j])) {
+          v[j] = w[j];
           pending &= ~(1u << j);
         }
       }
@@ -72,18 +67,15 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j < nin) {
-      const u32x2 y = u32x2{(uint32_t)v0[j], (uint32_t)v1[j]};
-      x = (lp || j > 0) ? VOp<DT, OP>::v2(x, y) : y;
+      const u32x4 y = Slot<kLineWide>::payload(v[j]);
+      x = (lp || j > 0) ? reduce_payload<DT, OP, F::PD>(x, y) : y;
     }
   }
+  drain_loads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j < nout) {
-      st_relaxed(fout[j] + 2 * li, ((uint64_t)flag_out[j] << 32) | x.x);
-      st_relaxed(fout[j] + 2 * li + 1, ((uint64_t)flag_out[j] << 32) | x.y);
-    }
-  }
-  if (op) store_payload<DT>(op + (int64_t)li * 8, x, valid, vec_ok);
+  for (int j = 0; j < 2; ++j)
+    if (j < nout) fout[j].store(li, x, flag_out[j]);
+  if (op) store_user<DT, F::PD>(op + (int64_t)li * F::PB, make_rsrc(op, nbytes), li * F::PB, x, valid, vec_ok);
 }
 
 // One workgroup per (rank, tree, channel, role). Role 0 folds the rank's own
@@ -94,7 +86,7 @@ __device__ __forceinline__ void tree_lines(int nlines, int64_t nbytes, const cha
 // channel; its producer owns `tail`, its consumer `head`, and a line's flag
 // is the low 32 bits of (step + 1).
 template <int DT, int OP>
-__global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
+__global__ void __launch_bounds__(kThreads) tree_line_kernel(TreeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int64_t E = sizeof(T);
   constexpr int64_t A = 16 / E;
@@ -108,7 +100,8 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
   if (role == 1 && root) return;  // the root's up pass starts the broadcast
   const Range cr = tree_channel_range(a.count, t, c, a.nchannels, A);
   if (cr.hi <= cr.lo) return;
-  const int64_t slice = (a.slot_bytes / 2) / E;  // one payload word pair per thread
+  using F = LineFmt<kLineWide, DT>;
+  const int64_t slice = (int64_t)kThreads * F::PB / E;  // one line per thread
   const int64_t nsl = div_up(cr.hi - cr.lo, slice);
 
   // FIFOs on each side, in child-slot order; unused entries stay null.
@@ -140,15 +133,15 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
     out_f[0] = kA >= 0 ? fifo_of(kA, 1) : -1;
     out_f[1] = kB >= 0 ? fifo_of(kB, 1) : -1;
   }
-  const int64_t fifo_words = (int64_t)a.nslots * a.slot_bytes / 8;
-  const uint64_t* in_fifo[2];
-  uint64_t* out_fifo[2];
+  const int64_t fifo_bytes = (int64_t)a.nslots * a.slot_bytes;
+  const char* in_fifo[2];
+  const char* out_fifo[2];
   FifoCtr* in_ctr[2];
   FifoCtr* out_ctr[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    in_fifo[j] = in_f[j] >= 0 ? reinterpret_cast<const uint64_t*>(a.fifo) + in_f[j] * fifo_words : nullptr;
-    out_fifo[j] = out_f[j] >= 0 ? reinterpret_cast<uint64_t*>(a.fifo) + out_f[j] * fifo_words : nullptr;
+    in_fifo[j] = in_f[j] >= 0 ? a.fifo + in_f[j] * fifo_bytes : nullptr;
+    out_fifo[j] = out_f[j] >= 0 ? a.fifo + out_f[j] * fifo_bytes : nullptr;
     in_ctr[j] = in_f[j] >= 0 ? a.ctr + in_f[j] : nullptr;
     out_ctr[j] = out_f[j] >= 0 ? a.ctr + out_f[j] : nullptr;
   }
@@ -209,14 +202,13 @@ __global__ void __launch_bounds__(kThreads) tree_flag_kernel(TreeArgs a) {
     }
     const int64_t n = min64(slice, cr.hi - cr.lo - s * slice);
     const int64_t nbytes = n * E;
-    const int nlines = (int)div_up(nbytes, 8);
-    const uint64_t* fin[2];
-    uint64_t* fout[2];
+    const int nlines = (int)div_up(nbytes, (int64_t)F::PB);
+    Slot<kLineWide> fin[2], fout[2];
     uint32_t flag_in[2], flag_out[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      fin[j] = j < nin ? in_fifo[j] + (int64_t)in_slot[j] * (a.slot_bytes / 8) : nullptr;
-      fout[j] = j < nout ? out_fifo[j] + (int64_t)out_slot[j] * (a.slot_bytes / 8) : nullptr;
+      fin[j].init(j < nin ? in_fifo[j] + (int64_t)in_slot[j] * a.slot_bytes : nullptr, a.slot_bytes);
+      fout[j].init(j < nout ? out_fifo[j] + (int64_t)out_slot[j] * a.slot_bytes : nullptr, a.slot_bytes);
       flag_in[j] = (uint32_t)(in_base[j] + s + 1);
       flag_out[j] = (uint32_t)(out_base[j] + s + 1);
     }

@@ -99,8 +99,8 @@ def test_tree_maximum_ranks(dtype):
 
 
 def test_tree_many_slices_flow_control():
-    """4 MiB per rank over 4 tree channels: 256 slices of 2 KiB per channel,
-    32 times the FIFO depth, so every producer waits on its consumer's head."""
+    """4 MiB per rank over 4 tree channels: 171 steps of 3 KiB per channel,
+    21 times the FIFO depth, so every producer waits on its consumer's head."""
     n, count = 8, 1 << 20
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
@@ -199,19 +199,20 @@ def test_tree_degenerate_shapes():
 
 @pytest.mark.parametrize("dtype", ["int32", "bfloat16", "int64"])
 def test_tree_channel_and_slice_boundaries(dtype):
-    """A channel carries its share of a tree's half in slices of 2 KiB (one
-    16-byte flag line per thread). Tree 0 takes the larger half; a half of
-    exactly one slice takes one channel and one 16-byte vector more takes
-    two; a half of exactly four slices fills the four channels with one
-    slice each and one vector more gives the first channel a second, short
-    slice. Every case must be whole and bit-exact."""
+    """A channel carries its share of a tree's half in steps of one WIDE line
+    per thread: 3 KiB of payload (2 KiB for int64). Tree 0 takes the larger
+    half; a half of exactly one step takes one channel and one 16-byte
+    vector more takes two; a half of exactly four steps fills the four
+    channels with one step each and one vector more gives the first channel
+    a second, short step. Every case must be whole and bit-exact."""
     e = {"int32": 4, "bfloat16": 2, "int64": 8}[dtype]
+    step_bytes = 256 * (8 if e == 8 else 12)
     n = 8
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
-        for slices, channels in ((1, (1, 2)), (4, (4, 4))):
+        for steps, channels in ((1, (1, 2)), (4, (4, 4))):
             for extra, want_channels in zip((0, 16 // e), channels):
-                count = 2 * (slices * 2048 // e + extra)
+                count = 2 * (steps * step_bytes // e + extra)
                 xs = _inputs(n, count, dtype, 1600 + count)
                 G.say(f"tree boundary {dtype} count={count}")
                 got = _run(comm, xs, dtype, "sum")
