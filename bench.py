@@ -669,6 +669,7 @@ def main() -> int:
             "t_median_us": round(t_med * 1e6, 2),
             "t_p95_us": round(t_p95 * 1e6, 2),
             "cv": round(cv, 4),
+            "cv_above_5pct": cv > 0.05,
             "frac_compulsory": round(compulsory / t_avg / 1e9 / HBM_PEAK_GBS, 4),
             "d2d_copy_gbs": round(d2d, 1),
             "cache_resident_copy_gbs": round(cache_copy, 1),
