@@ -237,23 +237,31 @@ def _ptr_array(bufs: Sequence) -> ctypes.Array:
     return (ctypes.c_void_p * len(bufs))(*[b if isinstance(b, int) else b.data_ptr() for b in bufs])
 
 
-def _marshal(comm: Comm, sendbufs, recvbufs, dtype):
+def _marshal(comm: Comm, sendbufs, recvbufs, dtype, send_need=None, recv_need=None):
+    """Pointer arrays and the dtype code. Tensor buffers must be contiguous
+    device tensors of one dtype (the given one, if any) holding at least
+    `send_need` / `recv_need` elements; raw addresses are taken as they are."""
     if len(sendbufs) != comm.nranks or len(recvbufs) != comm.nranks:
         raise ValueError(f"need {comm.nranks} send and receive buffers")
+    tensors = [b for b in list(sendbufs) + list(recvbufs) if not isinstance(b, int)]
     if dtype is None:
-        first = sendbufs[0]
-        if isinstance(first, int):
+        if isinstance(sendbufs[0], int):
             raise ValueError("dtype is required with raw pointers")
-        dtype = _dtype_name(first)
-        tdt = first.dtype
-        for bufs in (sendbufs, recvbufs):
+        dtype = _dtype_name(sendbufs[0])
+    code = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    for b in tensors:
+        if DTYPES.get(_dtype_name(b)) != code:
+            raise TypeError("all buffers must share the call's dtype")
+        if not b.is_cuda:
+            raise ValueError("buffers must be device tensors")
+        if not b.is_contiguous():
+            raise ValueError("buffers must be contiguous")
+    for bufs, need in ((sendbufs, send_need), (recvbufs, recv_need)):
+        if need is not None:
             for b in bufs:
-                if not isinstance(b, int):
-                    if b.dtype != tdt:
-                        raise TypeError("all buffers must share one dtype")
-                    if not b.is_cuda:
-                        raise ValueError("buffers must be device tensors")
-    return _ptr_array(sendbufs), _ptr_array(recvbufs), DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+                if not isinstance(b, int) and b.numel() < need:
+                    raise ValueError(f"a buffer holds {b.numel()} elements, the call needs {need}")
+    return _ptr_array(sendbufs), _ptr_array(recvbufs), code
 
 
 def _current_stream() -> int:
@@ -282,29 +290,29 @@ def _numel(b) -> int:
 
 def allreduce(comm: Comm, sendbufs, recvbufs, count: int | None = None, op: str | int = "sum",
               stream=None, dtype=None) -> None:
-    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype)
     n = _numel(sendbufs[0]) if count is None else count
+    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype, n, n)
     o = OPS[op] if isinstance(op, str) else int(op)
     _check(lib().ringsim_allreduce(comm, s, r, n, dt, o, _stream(stream)), "ringsim_allreduce")
 
 
 def reduce_scatter(comm: Comm, sendbufs, recvbufs, recvcount: int | None = None, op: str | int = "sum",
                    stream=None, dtype=None) -> None:
-    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype)
     n = _numel(recvbufs[0]) if recvcount is None else recvcount
+    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype, n * comm.nranks, n)
     o = OPS[op] if isinstance(op, str) else int(op)
     _check(lib().ringsim_reduce_scatter(comm, s, r, n, dt, o, _stream(stream)), "ringsim_reduce_scatter")
 
 
 def all_gather(comm: Comm, sendbufs, recvbufs, sendcount: int | None = None, stream=None, dtype=None) -> None:
-    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype)
     n = _numel(sendbufs[0]) if sendcount is None else sendcount
+    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype, n, n * comm.nranks)
     _check(lib().ringsim_all_gather(comm, s, r, n, dt, _stream(stream)), "ringsim_all_gather")
 
 
 def alltoall(comm: Comm, sendbufs, recvbufs, count: int | None = None, stream=None, dtype=None) -> None:
-    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype)
     n = _numel(sendbufs[0]) // comm.nranks if count is None else count
+    s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype, n * comm.nranks, n * comm.nranks)
     _check(lib().ringsim_alltoall(comm, s, r, n, dt, _stream(stream)), "ringsim_alltoall")
 
 

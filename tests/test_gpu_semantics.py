@@ -162,9 +162,23 @@ def test_bad_device_arguments():
         with pytest.raises(rs.RingsimError) as ei:  # all-to-all cannot run in place
             rs.alltoall(comm, t, t)
         assert ei.value.code == 4
+        # tensor buffers the binding refuses before anything is launched
+        with pytest.raises(ValueError):  # a count past the end of a buffer
+            rs.allreduce(comm, t, t, count=65)
+        with pytest.raises(ValueError):  # reduce-scatter input smaller than N x recvcount
+            rs.reduce_scatter(comm, t, [torch.zeros(64, device="cuda:0") for _ in range(2)])
+        with pytest.raises(ValueError):  # all-gather output smaller than N x sendcount
+            rs.all_gather(comm, t, [torch.zeros(100, device="cuda:0") for _ in range(2)])
+        with pytest.raises(ValueError):  # strided view
+            rs.allreduce(comm, [x[::2] for x in t], [x[::2] for x in t])
+        with pytest.raises(TypeError):  # tensors of another dtype than the call's
+            rs.allreduce(comm, t, t, dtype="int32")
+        with pytest.raises(ValueError):  # host tensors
+            rs.allreduce(comm, [x.cpu() for x in t], [x.cpu() for x in t])
         G.sync()
         assert rs.get_async_error(comm) == rs.SUCCESS
         info = rs.comm_query(comm)
         assert info["nranks"] == 2 and info["compute_units"] > 0
+        assert info["calls"] == 0
     finally:
         rs.comm_destroy(comm)
