@@ -59,9 +59,9 @@ struct RingModel {
   // Double-binary tree (WIDE lines, one line per thread per step): base,
   // per hop a + b * lines / 256, and per further step (scaled by the load of
   // its workgroups on the compute units once that passes one).
-  double tree_base_us = 6.73;
-  double tree_hop_us[2] = {0.833, 0.018};
-  double tree_step_us = 1.127;
+  double tree_base_us = 6.89;
+  double tree_hop_us[2] = {0.802, 0.030};
+  double tree_step_us = 1.072;
 };
 
 enum ModelColl : int { kModelAllReduce = 0, kModelReduceScatter = 1, kModelAllGather = 2 };
@@ -126,7 +126,7 @@ inline double line_model_us(const RingModel& m, int coll, int nranks, int nchann
 // tree's half of the buffer is split over `tree_channels` channels, and the
 // 4 x N x tree_channels workgroups (two trees, an up and a down role each)
 // share `cus` compute units. Fitted to the tree's own sweeps at 16, 8 and 4
-// ranks, sum and max, 1 KiB to 1 MiB per rank (within 6%).
+// ranks, sum and max, 1 KiB to 1 MiB per rank (within 5%).
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double slice_bytes,
                             double line_payload, double bytes_per_rank, int cus) {
   if (nranks <= 1) return m.base_us;

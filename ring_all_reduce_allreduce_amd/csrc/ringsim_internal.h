@@ -100,7 +100,7 @@ struct TreeArgs {
   uint64_t timeout_ticks;
 };
 
-constexpr int kTreeSlots = 8;
+constexpr int kTreeSlots = 16;
 // One 16-byte WIDE line per thread: every step of a tree workgroup is a
 // single load, fold and store per thread, the shortest path from a child's
 // flag to the parent's store.
