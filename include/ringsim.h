@@ -131,8 +131,9 @@ typedef enum {
  * moves WIDE lines (12 payload bytes and the flag in one 16-byte line, 8
  * payload bytes for int64), one line per thread and FIFO step, so a step
  * carries 3 KiB (2 KiB for int64). Each half is split over channels of one
- * step each, as many as allow one tree workgroup per compute unit
- * (4 x N x channels <= CUs); longer channels pipeline step by step. The tree
+ * step each, as many as allow one, or two, tree workgroups per compute unit
+ * (4 x N x channels <= CUs, or 2 x CUs), whichever the cost model predicts
+ * faster; longer channels pipeline step by step. The tree
  * needs 2*log2(N) dependent hops instead of the ring's 2(N-1). AUTO takes
  * the tree only where the fold order cannot change a result bit (integer
  * types, and max/min of any type) and the cost model predicts it faster;
@@ -185,7 +186,7 @@ typedef struct {
   uint64_t calls;              /* collective calls enqueued so far */
   int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG/WIDE, 0 if none */
   int algo;                    /* configured all-reduce algorithm (ringsim_algo_t) */
-  int tree_channels;           /* channels per tree in the tree FIFOs; a call takes at most CUs / (4N) */
+  int tree_channels;           /* channels per tree in the tree FIFOs; a call takes at most 2 CUs / (4N) */
   size_t tree_fifo_bytes;      /* double-tree FIFO bytes in HBM */
   int last_algo;               /* algorithm of the latest all-reduce: RINGSIM_ALGO_RING/TREE, 0 if none */
   int line_max_workgroups_per_channel; /* most workgroups per channel a FLAG/WIDE launch may take */
@@ -288,9 +289,9 @@ ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
 /* Host-only cost model of the tree all-reduce with `tree_channels` channels
  * per tree and `bytes_per_rank` bytes per rank of a 4-byte type on a 256-CU
  * device: base + 2 x tree depth x the per-hop latency of one step (one WIDE
- * line per thread) + the load of the tree's workgroups on the compute units
- * + one further step per further 3 KiB of a channel. Writes the predicted
- * microseconds. */
+ * line per thread) + one further step per further 3 KiB of a channel, hops
+ * and steps growing with the tree's workgroups per compute unit beyond one.
+ * Writes the predicted microseconds. */
 ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us);
 
 /* Host-only view of the partition used by the kernels. For `coll`

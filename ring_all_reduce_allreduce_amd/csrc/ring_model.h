@@ -57,11 +57,13 @@ struct RingModel {
   double line_crowd = 0.368;
   double line_gbs = 4540.0;
   // Double-binary tree (WIDE lines, one line per thread per step): base,
-  // per hop a + b * lines / 256, and per further step (scaled by the load of
-  // its workgroups on the compute units once that passes one).
-  double tree_base_us = 6.89;
-  double tree_hop_us[2] = {0.802, 0.030};
-  double tree_step_us = 1.072;
+  // per hop a + b * lines / 256, per further step, and how much each grows
+  // per workgroup per compute unit beyond the first.
+  double tree_base_us = 7.152;
+  double tree_hop_us[2] = {0.762, 0.069};
+  double tree_step_us = 1.037;
+  double tree_hop_crowd = 0.168;
+  double tree_step_crowd = 0.41;
 };
 
 enum ModelColl : int { kModelAllReduce = 0, kModelReduceScatter = 1, kModelAllGather = 2 };
@@ -125,17 +127,20 @@ inline double line_model_us(const RingModel& m, int coll, int nranks, int nchann
 // slice of `slice_bytes` per step in lines of `line_payload` bytes; each
 // tree's half of the buffer is split over `tree_channels` channels, and the
 // 4 x N x tree_channels workgroups (two trees, an up and a down role each)
-// share `cus` compute units. Fitted to the tree's own sweeps at 16, 8 and 4
-// ranks, sum and max, 1 KiB to 1 MiB per rank (within 5%).
+// share `cus` compute units: beyond one workgroup per unit, hops and steps
+// slow down in proportion. Fitted to the tree's own sweeps at 16, 8 and 4
+// ranks with one and two workgroups per unit, 1 KiB to 2 MiB per rank
+// (within 6%).
 inline double tree_model_us(const RingModel& m, int nranks, int depth, int tree_channels, double slice_bytes,
                             double line_payload, double bytes_per_rank, int cus) {
   if (nranks <= 1) return m.base_us;
   const double per_channel = std::ceil(bytes_per_rank / 2.0 / tree_channels);
   const double lines = std::ceil(std::min(per_channel, slice_bytes) / line_payload);
   const double steps = std::max(1.0, std::ceil(per_channel / slice_bytes));
-  const double load = 4.0 * nranks * tree_channels / cus;
-  return m.tree_base_us + 2.0 * depth * (m.tree_hop_us[0] + m.tree_hop_us[1] * lines / 256.0) +
-         (steps - 1.0) * m.tree_step_us * std::max(1.0, load);
+  const double extra = std::max(0.0, 4.0 * nranks * tree_channels / cus - 1.0);
+  return m.tree_base_us +
+         2.0 * depth * (m.tree_hop_us[0] + m.tree_hop_us[1] * lines / 256.0) * (1.0 + m.tree_hop_crowd * extra) +
+         (steps - 1.0) * m.tree_step_us * (1.0 + m.tree_step_crowd * extra);
 }
 
 }  // namespace ringsim

@@ -362,21 +362,29 @@ ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void*
 // int64).
 int64_t tree_slice_bytes(int esize) { return (int64_t)kThreads * (esize == 8 ? 8 : 12); }
 
-// Tree channels of one all-reduce: one slice of the half buffer its tree owns
-// per channel, and at most one tree workgroup per compute unit: with more,
-// the steps of the workgroups that share a unit queue behind each other and
-// a longer pipeline per channel is faster.
-int tree_channels_for(const ringsim_comm* c, size_t bytes_per_rank, int esize) {
-  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), tree_slice_bytes(esize));
-  const int64_t per_cu_cap = std::max<int64_t>(1, c->compute_units / (4 * (int64_t)c->nranks));
-  return (int)std::max<int64_t>(1, std::min<int64_t>({want, per_cu_cap, (int64_t)c->tree_channels}));
-}
+// Tree channels of one all-reduce and the predicted time: one step of the
+// half buffer its tree owns per channel, with at most one or two tree
+// workgroups per compute unit, whichever the cost model predicts faster
+// (two pay off once every channel pipelines several steps).
+struct TreePlan {
+  int channels;
+  double us;
+};
 
-double tree_predict_us(const ringsim_comm* c, size_t bytes_per_rank, int esize) {
+TreePlan tree_plan(const ringsim_comm* c, size_t bytes_per_rank, int esize) {
   const RingModel m;
   const int64_t slice = tree_slice_bytes(esize);
-  return tree_model_us(m, c->nranks, c->tree_depth, tree_channels_for(c, bytes_per_rank, esize), (double)slice,
-                       (double)(slice / kThreads), (double)bytes_per_rank, c->compute_units);
+  const int64_t want = div_up((int64_t)(bytes_per_rank / 2), slice);
+  TreePlan best{0, 0.0};
+  for (int per_cu = 1; per_cu <= 2; ++per_cu) {
+    const int64_t cap = std::max<int64_t>(1, per_cu * (int64_t)c->compute_units / (4 * (int64_t)c->nranks));
+    const int ch = (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, (int64_t)c->tree_channels}));
+    if (ch == best.channels) continue;
+    const double us = tree_model_us(m, c->nranks, c->tree_depth, ch, (double)slice, (double)(slice / kThreads),
+                                    (double)bytes_per_rank, c->compute_units);
+    if (best.channels == 0 || us < best.us) best = TreePlan{ch, us};
+  }
+  return best;
 }
 
 // AUTO's algorithm: the tree only where the fold order cannot show in the
@@ -387,8 +395,7 @@ bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t count) {
   const bool order_free = dtype == RINGSIM_INT32 || dtype == RINGSIM_INT64 || op == RINGSIM_MAX || op == RINGSIM_MIN;
   const bool lines_ok = c->proto != RINGSIM_PROTO_BULK;
   if (!order_free || !lines_ok || c->tree_channels < 1) return false;
-  return tree_predict_us(c, count * (size_t)dtype_size(dtype), dtype_size(dtype)) <
-         pick_proto(c, kAllReduce, count, dtype).us;
+  return tree_plan(c, count * (size_t)dtype_size(dtype), dtype_size(dtype)).us < pick_proto(c, kAllReduce, count, dtype).us;
 }
 
 ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const* rb, size_t count, int dtype,
@@ -401,7 +408,7 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   }
   a.count = (int64_t)count;
   a.nranks = c->nranks;
-  a.nchannels = tree_channels_for(c, count * (size_t)dtype_size(dtype), dtype_size(dtype));
+  a.nchannels = tree_plan(c, count * (size_t)dtype_size(dtype), dtype_size(dtype)).channels;
   c->last_tree_channels = a.nchannels;
   a.ch_stride = c->tree_channels;
   a.nslots = kTreeSlots;
