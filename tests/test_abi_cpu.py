@@ -63,6 +63,16 @@ def test_binding_mirrors_the_header():
     assert int(macros["MAX_WORKGROUPS_PER_CHANNEL"]) == rs.MAX_WORKGROUPS_PER_CHANNEL
 
 
+def test_tree_model_workgroups_per_cu(L):
+    """The tree's cost model, as measured at 16 ranks on 256 CUs: a second
+    tree workgroup per compute unit (8 channels instead of 4) loses while
+    each channel holds a few steps (64 KiB per rank) and wins once every
+    channel pipelines many (512 KiB and up)."""
+    assert rs.debug_tree_model(16, 4, 64 << 10) < rs.debug_tree_model(16, 8, 64 << 10)
+    for size in (512 << 10, 1 << 20, 4 << 20):
+        assert rs.debug_tree_model(16, 8, size) < rs.debug_tree_model(16, 4, size)
+
+
 def test_error_strings(L):
     for code in (0, 1, 2, 3, 4, 5, 7, 8):
         assert rs.error_string(code)
