@@ -186,7 +186,7 @@ typedef struct {
   uint64_t calls;              /* collective calls enqueued so far */
   int last_proto;              /* protocol of the latest ring call: RINGSIM_PROTO_BULK/FLAG/WIDE, 0 if none */
   int algo;                    /* configured all-reduce algorithm (ringsim_algo_t) */
-  int tree_channels;           /* channels per tree in the tree FIFOs; a call takes at most 2 CUs / (4N) */
+  int tree_channels;           /* channels per tree in the tree FIFOs (up to 2 x nchannels); a call takes at most 2 CUs / (4N) */
   size_t tree_fifo_bytes;      /* double-tree FIFO bytes in HBM */
   int last_algo;               /* algorithm of the latest all-reduce: RINGSIM_ALGO_RING/TREE, 0 if none */
   int line_max_workgroups_per_channel; /* most workgroups per channel a FLAG/WIDE launch may take */

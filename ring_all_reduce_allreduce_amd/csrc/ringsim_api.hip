@@ -601,11 +601,14 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   const int slices = (int)div_up((int64_t)stage_bytes, (int64_t)cfg.slot_bytes);
   const int nslots = std::max(cfg.nslots, 2 * slices);
 
-  // Tree channels: every workgroup of a tree launch (4 per rank and channel)
-  // must be resident at once, like the ring's.
+  // Tree channels: up to two per ring channel (a channel only splits a
+  // tree's range further and never changes a value), and every workgroup of
+  // a tree launch (4 per rank and channel) must be resident at once, like
+  // the ring's.
   const int tree_per_cu = tree_blocks_per_cu();
   const int64_t tree_resident = (int64_t)tree_per_cu * cus;
-  const int tree_channels = nranks < 2 ? 0 : (int)std::min<int64_t>(nchannels, tree_resident / (4 * (int64_t)nranks));
+  const int tree_channels =
+      nranks < 2 ? 0 : (int)std::min<int64_t>(2 * (int64_t)nchannels, tree_resident / (4 * (int64_t)nranks));
   if (cfg.algo == RINGSIM_ALGO_TREE && nranks > 1 && tree_channels < 1) return RINGSIM_INVALID_USAGE;
 
   ringsim_comm* c = new (std::nothrow) ringsim_comm();

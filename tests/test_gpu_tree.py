@@ -83,8 +83,8 @@ def test_tree_matrix(dtype):
 @pytest.mark.parametrize("dtype", ["float32", "int32"])
 def test_tree_maximum_ranks(dtype):
     """RINGSIM_MAX_RANKS (64) ranks: trees of depth 6 in which every rank is
-    a leaf of exactly one of the two trees, one tree channel per call (64
-    ranks x 4 workgroups already fill the device)."""
+    a leaf of exactly one of the two trees, one or two tree channels per
+    call (64 ranks x 4 workgroups already fill the device once)."""
     n = rs.MAX_RANKS
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
@@ -99,12 +99,13 @@ def test_tree_maximum_ranks(dtype):
 
 
 def test_tree_many_slices_flow_control():
-    """4 MiB per rank over 4 tree channels: 171 steps of 3 KiB per channel,
-    21 times the FIFO depth, so every producer waits on its consumer's head."""
+    """4 MiB per rank over 8 tree channels (two per ring channel): 86 steps
+    of 3 KiB per channel, five times the FIFO depth, so every producer waits
+    on its consumer's head."""
     n, count = 8, 1 << 20
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
-        assert rs.comm_query(comm)["tree_channels"] == 4
+        assert rs.comm_query(comm)["tree_channels"] == 8
         for dtype in ("float32", "int32"):
             xs = _inputs(n, count, dtype, 99)
             G.say(f"tree flow control N={n} count={count} dtype={dtype}")
@@ -202,15 +203,16 @@ def test_tree_channel_and_slice_boundaries(dtype):
     """A channel carries its share of a tree's half in steps of one WIDE line
     per thread: 3 KiB of payload (2 KiB for int64). Tree 0 takes the larger
     half; a half of exactly one step takes one channel and one 16-byte
-    vector more takes two; a half of exactly four steps fills the four
-    channels with one step each and one vector more gives the first channel
-    a second, short step. Every case must be whole and bit-exact."""
+    vector more takes two; a half of exactly eight steps fills the eight
+    tree channels (two per ring channel) with one step each and one vector
+    more gives the first channel a second, short step. Every case must be
+    whole and bit-exact."""
     e = {"int32": 4, "bfloat16": 2, "int64": 8}[dtype]
     step_bytes = 256 * (8 if e == 8 else 12)
     n = 8
     comm = rs.comm_init(n, 4, "auto", algo="tree")
     try:
-        for steps, channels in ((1, (1, 2)), (4, (4, 4))):
+        for steps, channels in ((1, (1, 2)), (8, (8, 8))):
             for extra, want_channels in zip((0, 16 // e), channels):
                 count = 2 * (steps * step_bytes // e + extra)
                 xs = _inputs(n, count, dtype, 1600 + count)
