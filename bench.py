@@ -153,18 +153,20 @@ def oracle_call(w: dict, xs):
     return oracle.alltoall(xs, w["dtype"])
 
 
-def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 10.0) -> dict:
+def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 10.0):
     """The oracle, as it stands, timed on this host on the same workload:
     whole calls, repeated until about `budget_s` seconds of CPU work (at
-    least three calls), median per call."""
+    least three calls), median per call. Returns the baseline record and the
+    oracle's result, against which the GPU result is then checked."""
     import numpy as np  # noqa: F401
 
     times = []
     t_start = time.perf_counter()
     c_start = time.process_time()
+    result = None
     while len(times) < 3 or time.perf_counter() - t_start < budget_s:
         t0 = time.perf_counter()
-        oracle_call(w, xs)
+        result = oracle_call(w, xs)
         times.append(time.perf_counter() - t0)
     # Threads actually busy: process CPU time over wall time.
     busy = (time.process_time() - c_start) / max(time.perf_counter() - t_start, 1e-9)
@@ -179,7 +181,7 @@ def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 10.0) -> di
         "sample": f"the full workload ({w['desc']}), NumPy ring replay on one thread, median of {len(times)} "
                   f"whole calls ({sum(times):.1f} s, CPU time / wall time {busy:.2f}), {t * 1e3:.3f} ms per call; host has "
                   f"{len(os.sched_getaffinity(0))} cores available",
-    }
+    }, result
 
 
 def mixed_copy_gbs(stream_bytes: int, resident_bytes: int, trials: int = 7) -> float:
@@ -283,11 +285,12 @@ def size_sweep(args) -> int:
     protocol and line workgroups per size with the library's cost model, and
     each line reports what it ran. Sizes are bytes per rank: the all-reduce
     buffer, the reduce-scatter input, the all-gather output. Each size is
-    checked against the oracle on sampled elements."""
+    checked on sampled elements against the plain definition: for int32 the
+    wrapping sum and the maximum do not depend on the fold order, and an
+    all-gather output is its inputs."""
     import numpy as np
     import torch
 
-    import oracle
     import ring_all_reduce_allreduce_amd as rs
     import synth
 
@@ -319,21 +322,20 @@ def size_sweep(args) -> int:
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
-        # Sampled parity: element columns of every rank's input, reduced (or
-        # gathered) by the oracle, against the same elements of one rank's
-        # output.
+        # Sampled parity: element columns of every rank's input, reduced by
+        # definition (wrapping int32 sum, or maximum) or gathered, against the
+        # same elements of one rank's output.
         r = k % n
         m = part if coll != "all_gather" else nin
         idx = np.unique(np.linspace(0, m - 1, min(m, 4096)).astype(np.int64))
         tidx = torch.from_numpy(idx).cuda()
         if coll == "all_gather":
-            cols = [t[tidx].cpu().numpy() for t in send]
-            want = oracle.ring_all_gather(cols, "int32", nchannels=1)[r]
+            want = np.concatenate([t[tidx].cpu().numpy() for t in send])
             got = np.concatenate([recv[r][b * part + tidx].cpu().numpy() for b in range(n)])
         else:
             off = r * part if coll == "reduce_scatter" else 0
-            cols = [t[off + tidx].cpu().numpy() for t in send]
-            want = oracle.ring_allreduce(cols, args.sweep_op, "int32", nchannels=1)[0]
+            cols = np.stack([t[off + tidx].cpu().numpy() for t in send])
+            want = cols.max(axis=0) if args.sweep_op == "max" else cols.sum(axis=0, dtype=np.int32)
             got = recv[r][tidx].cpu().numpy()
         ok = bool(np.array_equal(got, want))
         steps = args.steps if size < (64 << 20) else max(5, args.steps // 4)
@@ -521,19 +523,6 @@ def main() -> int:
         log("[bench] warmup left the communicator in error state")
         return 1
 
-    # Correctness of the timed configuration against the oracle.
-    check = None
-    if not args.no_check:
-        want = oracle_call(w, xs)
-        ok = True
-        for r in range(n):
-            got = recv[r].view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" else recv[r].cpu().numpy()
-            ok &= bool(np.array_equal(got.view(np.uint8), np.asarray(want[r]).view(np.uint8)))
-        check = "bit-exact vs oracle" if ok else "MISMATCH vs oracle"
-        log(f"[bench] parity: {check}")
-        if not ok:
-            return 1
-
     # Timed region: K steps, per-launch HIP events on the launch stream. A
     # short device sleep goes first so that every timed launch is already
     # queued when the one before it ends: event intervals then hold device
@@ -603,25 +592,30 @@ def main() -> int:
     gk = args.graph_calls if args.graph_calls >= 0 else w.get("graph_calls", 0)
     if gk > 0:
         graph = graph_timing(call, gk, stream)
-        if check is not None:
-            ok = True
-            for r in range(n):
-                got = recv[r].view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" else recv[r].cpu().numpy()
-                ok &= bool(np.array_equal(got.view(np.uint8), np.asarray(want[r]).view(np.uint8)))
-            graph["parity"] = "bit-exact vs oracle" if ok else "MISMATCH vs oracle"
-            if not ok:
-                log("[bench] graph launches: MISMATCH vs oracle")
-                return 1
         if rs.get_async_error(comm) != rs.SUCCESS:
             log("[bench] graph launches left the communicator in error state")
             return 1
         log(f"[bench] graph of {gk} calls: {graph['us_per_call']:.2f} us per call")
 
+    # The CPU oracle, timed (the cpu_baseline leg); the GPU result of the
+    # last launch (timed, back to back or from the graph; every launch of a
+    # buffer set computes the same values) is then checked against its
+    # result bit for bit.
     cpu = None
+    check = "not checked (the oracle runs only in the cpu_baseline leg)"
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
-        cpu = cpu_baseline(w, xs, per_rank_bytes)
+        cpu, want = cpu_baseline(w, xs, per_rank_bytes)
         log(f"[bench] cpu baseline {cpu}")
+        if not args.no_check:
+            ok = True
+            for r in range(n):
+                got = recv[r].view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" else recv[r].cpu().numpy()
+                ok &= bool(np.array_equal(got.view(np.uint8), np.asarray(want[r]).view(np.uint8)))
+            check = "bit-exact vs oracle" if ok else "MISMATCH vs oracle"
+            log(f"[bench] parity: {check}")
+            if not ok:
+                return 1
 
     kernel_name = {"allreduce": "ring_bulk_kernel (all-reduce)", "reduce_scatter": "ring_bulk_kernel (reduce-scatter)",
                    "all_gather": "ring_bulk_kernel (all-gather)", "alltoall": "copy_kernel (all-to-all)"}[coll]
