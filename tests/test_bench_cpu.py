@@ -1,6 +1,6 @@
-"""Host-only checks of bench.py: the oracle is test infrastructure and runs
-in bench.py only in the cpu_baseline leg (its timed calls, whose result the
-GPU output is then checked against)."""
+"""Host-only checks that the oracle stays test infrastructure: bench.py
+runs it only in the cpu_baseline leg (its timed calls, whose result the GPU
+output is then checked against), and the product package never imports it."""
 import ast
 import os
 
@@ -35,3 +35,18 @@ def test_bench_runs_the_oracle_only_in_the_cpu_baseline_leg():
     assert not any(imports_oracle(node) for node in tree.body)
     assert _functions_using(tree, imports_oracle) == {"oracle_call"}
     assert _functions_using(tree, calls("oracle_call")) == {"cpu_baseline"}
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "ring_all_reduce_allreduce_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for name in files:
+            if not name.endswith(".py"):
+                continue
+            with open(os.path.join(dirpath, name)) as f:
+                tree = ast.parse(f.read())
+            for node in ast.walk(tree):
+                if isinstance(node, ast.Import):
+                    assert all(a.name.split(".")[0] != "oracle" for a in node.names), name
+                if isinstance(node, ast.ImportFrom):
+                    assert (node.module or "").split(".")[0] != "oracle", name
