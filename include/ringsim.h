@@ -194,7 +194,9 @@ typedef struct {
   int last_tree_channels;              /* channels per tree of the latest all-reduce, 0 if it ran the ring */
 } ringsim_comm_info_t;
 
-/* Fills *cfg with the defaults. Environment overrides, read by this call:
+/* Fills *cfg with the defaults ("NCCL" book, ch. 3, s. 3.5: every tunable is
+ * a named parameter with a default that an environment variable overrides,
+ * read once). Environment overrides, read by this call:
  * RINGSIM_CHUNK_BYTES, RINGSIM_WPC, RINGSIM_SLOT_BYTES, RINGSIM_NSLOTS,
  * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD, RINGSIM_ALGO, RINGSIM_LINE_WPC;
  * RINGSIM_DEBUG=WARN|INFO logs to stderr. Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
@@ -204,24 +206,38 @@ ringsim_result_t ringsim_config_default(ringsim_config_t* cfg);
 
 /* Creates a communicator of `nranks` (1..RINGSIM_MAX_RANKS) simulated ranks
  * on the current HIP device, with `nchannels` (1..RINGSIM_MAX_CHANNELS) ring
- * channels and protocol `proto` (ringsim_proto_t). Ring order is
- * r -> (r + 1) mod nranks. Allocates the FIFOs and counters in HBM once;
- * synchronous. On error *comm is left untouched: bad arguments give
+ * channels and protocol `proto` (ringsim_proto_t). Follows "NCCL" book,
+ * ch. 3, s. 3.1 (ncclCommInitRank: validate the rank count and arguments,
+ * then allocate the communicator and its abort flag with a device-visible
+ * copy) and s. 3.3 (commAlloc: the communicator's memory is allocated once,
+ * at init). Ring order is r -> (r + 1) mod nranks. Allocates the FIFOs,
+ * counters and the host-mapped abort and error words once; synchronous. On error *comm is left untouched: bad arguments give
  * RINGSIM_INVALID_ARGUMENT, a configuration whose workgroups cannot all be
  * resident at once gives RINGSIM_INVALID_USAGE, a failed HIP allocation
  * RINGSIM_UNHANDLED_DEVICE_ERROR. */
 ringsim_result_t ringsim_comm_init(ringsim_comm_t* comm, int nranks, int nchannels, int proto);
 
-/* As ringsim_comm_init with explicit tunables (cfg may be NULL). */
+/* As ringsim_comm_init with explicit tunables (cfg may be NULL), as
+ * ncclCommInitRankConfig takes a config next to the plain call ("NCCL" book,
+ * ch. 3, s. 3.1). Zero fields of *cfg take ringsim_config_default's value;
+ * *cfg is read during the call only and stays the caller's. */
 ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int nchannels, int proto,
                                           const ringsim_config_t* cfg);
 
 /* Waits for all work on the device (hipDeviceSynchronize: the streams the
  * communicator was used on may no longer exist), frees its device memory
- * and invalidates the handle. Not to be called while a stream that holds
- * its calls is being captured. */
+ * and invalidates the handle: its magic words are overwritten and it leaves
+ * the registry of live handles, so a later call with it returns
+ * RINGSIM_INVALID_USAGE instead of reading freed memory ("NCCL" book, ch. 2,
+ * s. 2.1: the use-after-destroy pitfall that startMagic/endMagic catch).
+ * Not to be called while a stream that holds its calls is being captured. */
 ringsim_result_t ringsim_comm_destroy(ringsim_comm_t comm);
 
+/* Copies the communicator's shape and the choices of its latest call into
+ * *info (caller-owned host memory). The fields mirror what ncclComm records
+ * per communicator ("NCCL" book, ch. 2, s. 2.1: rank count, channels, buffer
+ * sizes; s. 2.2: channel count). Host only; RINGSIM_INVALID_ARGUMENT for a
+ * NULL info, RINGSIM_INVALID_USAGE for a bad handle. */
 ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* info);
 
 /* Ring all-reduce ("AI Systems Performance Engineering (3)", collectives
@@ -232,27 +248,33 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
 ringsim_result_t ringsim_allreduce(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                    size_t count, int dtype, int op, ringsim_stream_t stream);
 
-/* Ring reduce-scatter (same table: each rank keeps one block of the
- * reduction). sendbufs[r] holds nranks * recvcount elements; recvbufs[r]
- * receives the reduced block r, folded in rank order r+1, ..., r. recvbufs[r]
- * may equal sendbufs[r] + r * recvcount elements (in place). */
+/* Ring reduce-scatter ("AI Systems Performance Engineering (3)", collectives
+ * table: each rank keeps one block of the reduction; "In-Network SHARP
+ * Aggregation": a rank receives (n-1)/n of the buffer). sendbufs[r] holds
+ * nranks * recvcount elements; recvbufs[r] receives the reduced block r,
+ * folded in rank order r+1, ..., r. recvbufs[r] may equal
+ * sendbufs[r] + r * recvcount elements (in place). */
 ringsim_result_t ringsim_reduce_scatter(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                         size_t recvcount, int dtype, int op, ringsim_stream_t stream);
 
-/* Ring all-gather (same table; slice order of "NCCL 专家课程 17", section
+/* Ring all-gather ("AI Systems Performance Engineering (3)", collectives
+ * table; slice order of "NCCL 专家课程 17", section
  * "Bootstrap Ring 与 AllGather"). sendbufs[r] holds sendcount elements;
  * block b of recvbufs[r] (nranks * sendcount elements) receives sendbufs[b].
  * sendbufs[r] may equal recvbufs[r] + r * sendcount elements (in place). */
 ringsim_result_t ringsim_all_gather(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                     size_t sendcount, int dtype, ringsim_stream_t stream);
 
-/* All-to-all (same table: chunk j of rank i goes to rank j). Both buffers of
+/* All-to-all ("AI Systems Performance Engineering (3)", collectives table:
+ * chunk j of rank i goes to rank j). Both buffers of
  * a rank hold nranks * count elements; block i of recvbufs[j] receives block
  * j of sendbufs[i]. Send and receive buffers must not overlap. */
 ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                   size_t count, int dtype, ringsim_stream_t stream);
 
-/* Reports the communicator's asynchronous state: RINGSIM_SUCCESS,
+/* Reports the communicator's asynchronous state ("NCCL" book, ch. 2, s. 2.1:
+ * the asyncResult field of ncclComm; s. 2.6: asyncResult becomes success when
+ * every channel is done, and ncclCommGetAsyncError reads it): RINGSIM_SUCCESS,
  * RINGSIM_IN_PROGRESS while enqueued work on the stream of the latest call
  * is still running and no error is known, or the error a kernel or
  * ringsim_abort left behind. While that stream is being captured into a
@@ -260,11 +282,16 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
  * are reported. */
 ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error);
 
-/* Raises the abort word that every spinning kernel polls; running kernels
- * stop waiting and finish, and every later call returns RINGSIM_ABORTED. */
+/* Raises the abort word that every spinning kernel polls ("NCCL" book, ch. 3,
+ * s. 3.1: the host abort flag and its device-visible copy; s. 3.2: every
+ * blocking loop checks the abort flag every so many spins); running kernels
+ * stop waiting and finish, and every later call returns RINGSIM_ABORTED.
+ * Host only, never blocks. */
 ringsim_result_t ringsim_abort(ringsim_comm_t comm);
 
-/* Static text for a result code. */
+/* Static text for a result code (the result names of "NCCL 专家课程 17:
+ * Bootstrap 与 Communicator 初始化状态机", failure experiments). The string is
+ * owned by the library and never freed. */
 const char* ringsim_get_error_string(ringsim_result_t result);
 
 /* Host-only cost model behind AUTO ("NCCL" book, ch. 5, ring.cc: latency =
@@ -283,10 +310,12 @@ ringsim_result_t ringsim_debug_model(int coll, int nranks, int nchannels, size_t
 
 /* Host-only tree shape. Writes links[6] = (parent, first child, second
  * child) of `rank` in tree 0, then the same in tree 1 (-1 = none), for a
- * double binary tree over `nranks` ranks ("NCCL" book, ch. 4). */
+ * double binary tree over `nranks` ranks ("NCCL" book, ch. 4, ncclGetBtree
+ * and ncclGetDtree). links is caller-owned host memory of 6 ints. */
 ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
 
-/* Host-only cost model of the tree all-reduce with `tree_channels` channels
+/* Host-only cost model ("NCCL" book, ch. 5, the tree latency and bandwidth
+ * terms) of the tree all-reduce with `tree_channels` channels
  * per tree and `bytes_per_rank` bytes per rank of a 4-byte type on a 256-CU
  * device: base + 2 x tree depth x the per-hop latency of one step (one WIDE
  * line per thread) + one further step per further 3 KiB of a channel, hops
@@ -294,7 +323,10 @@ ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
  * Writes the predicted microseconds. */
 ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us);
 
-/* Host-only view of the partition used by the kernels. For `coll`
+/* Host-only view of the partition used by the kernels ("NCCL" book, ch. 2,
+ * s. 2.2: a channel owns count / nChannels of the data; s. 2.3: a loop of
+ * nranks chunks, the ragged last loop's chunk size and the chunk visited at
+ * every stage). For `coll`
  * (ringsim_coll_t), writes rows of 5 int64 values
  *   (channel, loop, chunk, begin, end)
  * with [begin, end) absolute element indices: for the all-reduce, chunk k of

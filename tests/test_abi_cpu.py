@@ -243,3 +243,35 @@ def test_tree_model_shape(L):
         assert rs.debug_tree_model(n, c, 256 << 20) > big["bulk_us"]
     assert rs.debug_tree_model(16, 1, 8) - rs.debug_tree_model(8, 1, 8) < \
         rs.debug_model("allreduce", 16, 16, 8)["flag_us"] - rs.debug_model("allreduce", 8, 16, 8)["flag_us"]
+
+
+# Names by which the header cites the four pages the library follows.
+PAGE_MARKERS = ('"NCCL" book', "NCCL 专家课程 17", "NCCL 专家课程 29", "AI Systems Performance Engineering (3)")
+
+
+def _declared_with_comments():
+    """(function name, the comment block right above its declaration) for
+    every function include/ringsim.h declares."""
+    import re
+
+    with open(rs.HEADER_PATH) as f:
+        text = f.read()
+    out = []
+    for m in re.finditer(r"^(?:ringsim_result_t|const char\*)\s+(ringsim_[a-z_]+)\s*\(", text, re.M):
+        before = text[: m.start()].rstrip()
+        assert before.endswith("*/"), f"{m.group(1)} has no comment block above it"
+        out.append((m.group(1), before[before.rindex("/*"):]))
+    return out
+
+
+def test_every_export_cites_the_page_that_defines_it():
+    """Each declared call names, in the comment right above it, the page (and
+    its section) that defines what the call does; the allocation-free entry
+    point instead names the callers it serves."""
+    decls = _declared_with_comments()
+    assert {n for n, _ in decls} == set(rs.header_exports())
+    for name, comment in decls:
+        if name.endswith("_noalloc"):
+            assert "cannot allocate" in comment, name
+            continue
+        assert any(p in comment for p in PAGE_MARKERS), f"{name}: no page cited in {comment!r}"
