@@ -1,11 +1,11 @@
 // ring_bulk.hip -- the bulk ring kernel (Simple protocol, "NCCL" book,
 // s. 2.4): FIFO slots hold raw payload and readiness travels in separate
-// 64-bit step counters (tail: slots filled, head: slots drained), one pair per
-// FIFO and wave. Slot data is written and read with device-scope coherent
-// (SC1) accesses, so a counter published once those accesses have completed
-// is enough to order them; no L2 writeback or invalidate is needed. Workgroup
-// ids are rank-major, so that when the pipeline count is a multiple of 8
-// every workgroup of a pipeline is dispatched to the same XCD.
+// 64-bit step counters (tail: slots filled, head: slots drained). Slot data
+// is written and read with device-scope coherent (SC1) accesses, so a
+// counter published once those accesses have completed is enough to order
+// them; no L2 writeback or invalidate is needed. Workgroup ids are
+// rank-major, so that when the pipeline count is a multiple of 8 every
+// workgroup of a pipeline is dispatched to the same XCD.
 #include "ringsim_device.h"
 
 namespace ringsim {
@@ -144,18 +144,11 @@ __device__ __forceinline__ void move_slice(int64_t n, const char* fin, const cha
       else move_vec<DT, OP, false, false, true, false>(nv, rin, l4, rout, u4);
     }
   }
-  // Elements past the last whole vector, or all of them when user buffers
-  // are not 16-byte aligned. Every byte of a slot keeps one owner thread
-  // whatever a step's length, since each wave only knows that its own
-  // consumer has drained its own bytes: with vector moves, the elements past
-  // the last whole vector lie in vector nv and its owner (thread nv mod 256)
-  // moves them; without, element i always falls to thread i mod 256.
+  // Elements past the last whole vector (or all of them when user buffers
+  // are not 16-byte aligned).
   const T* l1 = reinterpret_cast<const T*>(loc);
   T* o1 = reinterpret_cast<T*>(uout);
-  const int64_t first = vec_ok ? nv * A : (int64_t)threadIdx.x;
-  const int64_t stride = vec_ok ? 1 : kThreads;
-  if (vec_ok && (n == nv * A || (int)(nv % kThreads) != (int)threadIdx.x)) return;
-  for (int64_t i = first; i < n; i += stride) {
+  for (int64_t i = nv * A + threadIdx.x; i < n; i += kThreads) {
     const int off = (int)(i * (int64_t)sizeof(T));
     T x = fin ? fifo_ld<T>(rin, off) : l1[i];
     if (fin && loc) x = VOp<DT, OP>::one(x, l1[i]);
@@ -181,21 +174,6 @@ __device__ __forceinline__ void stage_to_lds(const char* src, int64_t nv, u32x4*
   }
 }
 
-// Does wave `wave` own any element of an n-element step? Vectors are dealt
-// to threads in turn (vector i, whole or the partial last one, to thread
-// i mod 256; without vector moves element i to thread i mod 256), so a short
-// step leaves the later waves without work; sender and receiver of a step
-// compute the same answer, so both skip it together.
-__device__ __forceinline__ bool wave_has_part(int64_t n, int64_t A, int vec_ok, int wave) {
-  const int64_t units = vec_ok ? div_up(n, A) : n;
-  return units > (int64_t)wave * 64;
-}
-
-// Bulk ring kernel. Every wave of a workgroup is a pipeline of its own: it
-// moves the vectors of each step that fall to its 64 threads, with its own
-// tail and head counter per FIFO, and publishes as soon as its own stores
-// have completed. No barrier sits on a hop: a step costs the poll, the
-// loads, the stores and their acknowledgement of one wave.
 template <int DT, int OP, int MODE>
 __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
@@ -203,30 +181,29 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   extern __shared__ u32x4 lds_stage[];  // [2][slot_bytes / 16] when a.lds_stage
   const Pipe p = locate(a);
   if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
-  const int wave = (int)(threadIdx.x >> 6);
-  const bool lead = (threadIdx.x & 63) == 0;
-  // Counters of this wave: the pipeline's counter block holds kWaves of them.
-  FifoCtr* const in_ctr = a.ctr + ((int64_t)p.r * a.pipe_stride + p.pipe) * kWaves + wave;
-  FifoCtr* const out_ctr = a.ctr + ((int64_t)p.nxt * a.pipe_stride + p.pipe) * kWaves + wave;
-  uint64_t b_in = 0, b_out = 0;
-  if (lead) {
+  __shared__ uint64_t s_base[2];
+  if (threadIdx.x == 0) {
     // Each side's own counter tells where the previous call left this FIFO.
-    b_in = ld_relaxed(&in_ctr->head);
-    b_out = ld_relaxed(&out_ctr->tail);
+    s_base[0] = ld_relaxed(&p.in_ctr->head);
+    s_base[1] = ld_relaxed(&p.out_ctr->tail);
   }
-  const uint64_t in_base = uniform64(b_in);
-  const uint64_t out_base = uniform64(b_out);
+  __syncthreads();
+  const uint64_t in_base = uniform64(s_base[0]);
+  const uint64_t out_base = uniform64(s_base[1]);
   const uint64_t nslots = (uint64_t)a.nslots;
   const int64_t stage_vecs = a.slot_bytes / 16;
   uint64_t nrecv = 0, nsent = 0;
-  uint64_t known_tail = 0, known_head = 0;  // counter values this wave has seen
-  bool stop = false;                         // a wait gave up: stop waiting
+  uint64_t known_tail = 0, known_head = 0;  // meaningful in thread 0 only
+  bool stop = false;                         // thread 0: stop waiting
   const WaitCtx wc = wait_ctx(a);
   // Slot of the next receive / send: (base + count) mod nslots, advanced
   // without a division.
   uint32_t in_slot = (uint32_t)(in_base % nslots);
   uint32_t out_slot = (uint32_t)(out_base % nslots);
 
+  // Step groups (a.group > 0): a stage moves at most a.group slot steps
+  // before the next stage runs, so a FIFO of 2 x a.group slots suffices
+  // whatever the chunk size.
   const int64_t slice = a.slot_bytes / (int64_t)sizeof(T);
   StepIter<DT, MODE> it;
   it.init(a, p.r, p.c, p.w, slice, a.group > 0 ? (int64_t)a.group * slice : 0);
@@ -234,54 +211,52 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   if (!nx.done) nx.next();
   const bool lds = a.lds_stage && a.vec_ok;
   int buf = 0;
-  // Each thread stages, and later reads, only the vectors dealt to it, so a
-  // wave needs nothing of another wave's staging.
   if (lds && !it.done && it.use_local) {
     stage_to_lds(it.local(), it.ns() / A, lds_stage);
     wait_vmem();
+    __syncthreads();
   }
 
   while (!it.done) {
-    const int64_t ns = it.ns();
-    if (wave_has_part(ns, A, a.vec_ok, wave)) {
-      const bool recv = it.recv, send = it.send;
-      if (!stop && recv && known_tail < in_base + nrecv + 1) {
-        uint64_t v = 0;
-        if (lead) v = wait_geq(&in_ctr->tail, in_base + nrecv + 1, wc);
-        known_tail = uniform64(v);
+    const bool recv = it.recv, send = it.send;
+    if (threadIdx.x == 0 && !stop) {
+      // A counter value seen earlier may already cover this step. The
+      // barrier below keeps every thread's slot accesses after the wait.
+      const uint64_t need_tail = in_base + nrecv + 1;
+      if (recv && known_tail < need_tail) {
+        known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
         stop = known_tail == 0;
       }
-      if (!stop && send && nsent + 1 > nslots && known_head < out_base + nsent + 1 - nslots) {
-        uint64_t v = 0;
-        if (lead) v = wait_geq(&out_ctr->head, out_base + nsent + 1 - nslots, wc);
-        known_head = uniform64(v);
+      const uint64_t need_head = out_base + nsent + 1 - nslots;
+      if (!stop && send && nsent + 1 > nslots && known_head < need_head) {
+        known_head = wait_geq(&p.out_ctr->head, need_head, wc);
         stop = known_head == 0;
       }
-      const char* fin = recv ? p.in_fifo + (int64_t)in_slot * a.slot_bytes : nullptr;
-      char* fout = send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr;
-      move_slice<DT, OP>(ns, fin, it.use_local ? it.local() : nullptr, fout, it.store ? it.out() : nullptr,
-                         a.slot_bytes, a.vec_ok, lds && it.use_local ? lds_stage + buf * stage_vecs : nullptr);
-      // The next step's own operand streams into the other LDS buffer while
-      // this step's stores drain.
-      if (lds && !nx.done && nx.use_local) stage_to_lds(nx.local(), nx.ns() / A, lds_stage + (buf ^ 1) * stage_vecs);
-      // This wave's FIFO stores (device-coherent), FIFO loads and staging
-      // loads have completed before its lead lane publishes tail and head.
-      wait_vmem();
-      if (lead) {
-        if (send) st_relaxed(&out_ctr->tail, out_base + nsent + 1);
-        if (recv) st_relaxed(&in_ctr->head, in_base + nrecv + 1);
-      }
-      if (recv) {
-        ++nrecv;
-        in_slot = in_slot + 1 == (uint32_t)nslots ? 0 : in_slot + 1;
-      }
-      if (send) {
-        ++nsent;
-        out_slot = out_slot + 1 == (uint32_t)nslots ? 0 : out_slot + 1;
-      }
-    } else if (lds && !nx.done && nx.use_local) {
-      stage_to_lds(nx.local(), nx.ns() / A, lds_stage + (buf ^ 1) * stage_vecs);
-      wait_vmem();
+    }
+    __syncthreads();
+    const int64_t ns = it.ns();
+    const char* fin = recv ? p.in_fifo + (int64_t)in_slot * a.slot_bytes : nullptr;
+    char* fout = send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr;
+    move_slice<DT, OP>(ns, fin, it.use_local ? it.local() : nullptr, fout, it.store ? it.out() : nullptr,
+                       a.slot_bytes, a.vec_ok, lds && it.use_local ? lds_stage + buf * stage_vecs : nullptr);
+    // The next step's own operand streams into the other LDS buffer while
+    // this step's stores drain.
+    if (lds && !nx.done && nx.use_local) stage_to_lds(nx.local(), nx.ns() / A, lds_stage + (buf ^ 1) * stage_vecs);
+    // Every thread's FIFO stores (device-coherent), FIFO loads and staging
+    // loads have completed before thread 0 publishes the new tail and head.
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (send) st_relaxed(&p.out_ctr->tail, out_base + nsent + 1);
+      if (recv) st_relaxed(&p.in_ctr->head, in_base + nrecv + 1);
+    }
+    if (recv) {
+      ++nrecv;
+      in_slot = in_slot + 1 == (uint32_t)nslots ? 0 : in_slot + 1;
+    }
+    if (send) {
+      ++nsent;
+      out_slot = out_slot + 1 == (uint32_t)nslots ? 0 : out_slot + 1;
     }
     buf ^= 1;
     it = nx;

@@ -102,8 +102,6 @@ struct ringsim_comm {
   size_t flag_fifo_bytes;
   FifoCtr* ctr;
   size_t ctr_bytes;
-  FifoCtr* bulk_ctr;  // bulk counters: [rank][channel][part][wave]
-  size_t bulk_ctr_bytes;
   uint32_t* dev_abort;
   uint32_t* host_words;      // [0] abort request, [1] kernel error (host view)
   uint32_t* host_words_dev;  // the same words as the device sees them
@@ -222,9 +220,6 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int li
     a->group = kLineGroupSteps;
   } else {
     a->wpc = c->wpc;
-    a->ctr = c->bulk_ctr;
-    a->pipe_stride = c->nchannels * c->wpc;
-    a->pipe_mul = c->wpc;
     a->fifo = c->fifo;
     a->fifo_stride = c->nchannels * c->wpc;
     a->fifo_mul = c->wpc;
@@ -496,8 +491,6 @@ void free_comm_memory(ringsim_comm* c) {
   if (c->fifo) (void)hipFree(c->fifo);
   if (c->flag_fifo) (void)hipFree(c->flag_fifo);
   if (c->ctr) (void)hipFree(c->ctr);
-  if (c->bulk_ctr) (void)hipFree(c->bulk_ctr);
-  c->bulk_ctr = nullptr;
   if (c->tree_fifo) (void)hipFree(c->tree_fifo);
   if (c->tree_ctr) (void)hipFree(c->tree_ctr);
   c->tree_fifo = nullptr;
@@ -658,14 +651,12 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->fifo_bytes = (size_t)(nc * wpc) * nslots * cfg.slot_bytes;
   c->flag_fifo_bytes = (size_t)nc * line_fifo_per_nc;
   c->ctr_bytes = (size_t)(nc * c->pipe_mul) * sizeof(FifoCtr);
-  c->bulk_ctr_bytes = (size_t)(nc * wpc) * kWaves * sizeof(FifoCtr);
   const size_t tree_fifos = (size_t)2 * tree_channels * nranks * 2;
   c->tree_fifo_bytes = tree_fifos * kTreeSlots * kTreeSlotBytes;
   c->tree_ctr_bytes = tree_fifos * sizeof(FifoCtr);
   bool ok = hipMalloc((void**)&c->fifo, c->fifo_bytes) == hipSuccess &&
             hipMalloc((void**)&c->flag_fifo, c->flag_fifo_bytes) == hipSuccess &&
             hipMalloc((void**)&c->ctr, c->ctr_bytes) == hipSuccess &&
-            hipMalloc((void**)&c->bulk_ctr, c->bulk_ctr_bytes) == hipSuccess &&
             hipMalloc((void**)&c->dev_abort, 256) == hipSuccess &&
             hipHostMalloc((void**)&c->host_words, 256, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   if (ok) ok = hipHostGetDevicePointer((void**)&c->host_words_dev, c->host_words, 0) == hipSuccess;
@@ -678,7 +669,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Flags of the flag-packed FIFO start at zero, a value no step ever uses.
   if (ok) ok = hipMemset(c->flag_fifo, 0, c->flag_fifo_bytes) == hipSuccess &&
                hipMemset(c->ctr, 0, c->ctr_bytes) == hipSuccess &&
-               hipMemset(c->bulk_ctr, 0, c->bulk_ctr_bytes) == hipSuccess && hipMemset(c->dev_abort, 0, 256) == hipSuccess &&
+               hipMemset(c->dev_abort, 0, 256) == hipSuccess &&
                hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     free_comm_memory(c);

@@ -9,7 +9,6 @@
 namespace ringsim {
 
 constexpr int kThreads = 256;         // threads per workgroup (4 wave64)
-constexpr int kWaves = kThreads / 64;  // bulk: every wave is a pipeline with counters of its own
 constexpr int kUnroll = 8;            // 16-byte vectors in flight per thread
 constexpr int kDefaultSlotBytes = kThreads * 16 * kUnroll;  // 32 KiB: one pass per slot
 constexpr int kDefaultSlots = 8;      // FIFO depth (NCCL_STEPS)
@@ -65,7 +64,7 @@ struct RingArgs {
   int slot_bytes;
   int vec_ok;           // every user buffer is 16-byte aligned
   char* fifo;           // FIFO slots: [rank][pipeline][slot][slot_bytes]
-  FifoCtr* ctr;         // counters: [rank][pipeline] (bulk: [rank][pipeline][kWaves])
+  FifoCtr* ctr;         // counters: [rank][pipeline]
   uint32_t* dev_abort;  // device word: set when any workgroup gives up
   const uint32_t* host_abort;  // host-mapped word set by ringsim_abort
   uint32_t* host_err;   // host-mapped error word
