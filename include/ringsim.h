@@ -338,6 +338,30 @@ ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t 
 ringsim_result_t ringsim_debug_plan(int coll, size_t count, int nranks, int nchannels, size_t chunk_bytes,
                                     int dtype, int64_t* rows, size_t max_rows, size_t* nrows);
 
+/* Allocation-free ring all-reduce, for callers that cannot allocate device
+ * memory at call time (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Computes exactly what ringsim_allreduce
+ * computes on a communicator of `nranks` ranks and `nchannels` channels with
+ * the ring algorithm (the same chunks and fold order, so equal results bit
+ * for bit), with the bulk protocol, but needs no communicator: its FIFO
+ * slots, step counters and error words live in a library-owned scratch
+ * array in device memory, one copy per GPU (32 MiB plus 32 KiB, held until
+ * the process ends), set up on the first call on each device. Arguments as
+ * ringsim_allreduce; the caller passes the input and output buffers.
+ * Limits: nranks * nchannels <= 128 (larger shapes return
+ * RINGSIM_INVALID_ARGUMENT and log a warning with RINGSIM_DEBUG=WARN);
+ * chunk size from RINGSIM_CHUNK_BYTES as ringsim_config_default. Every call
+ * on one GPU shares that GPU's scratch and starts by clearing its counters
+ * with a small kernel: calls that may overlap on one GPU (unordered streams,
+ * other threads) race and give undefined results; order them on the device.
+ * No abort and no asynchronous error report: a wait that exceeds the
+ * RINGSIM_TIMEOUT_MS bound gives up, leaves the output undefined and is not
+ * reported (ringsim_allreduce on a communicator reports it). Calls no
+ * hipMalloc, hipFree or other allocating routine. */
+ringsim_result_t ringsim_allreduce_noalloc(int nranks, int nchannels, const void* const* sendbufs,
+                                           void* const* recvbufs, size_t count, int dtype, int op,
+                                           ringsim_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,7 @@ Functions carry the C names without the ``ringsim_`` prefix:
 
     comm = comm_init(nranks, nchannels, proto="auto", **config)
     allreduce(comm, sendbufs, recvbufs, count=None, op="sum", stream=None)
+    allreduce_noalloc(nranks, nchannels, sendbufs, recvbufs, count=None, op="sum", stream=None)
     reduce_scatter(comm, sendbufs, recvbufs, recvcount=None, op="sum", stream=None)
     all_gather(comm, sendbufs, recvbufs, sendcount=None, stream=None)
     alltoall(comm, sendbufs, recvbufs, count=None, stream=None)
@@ -141,6 +142,7 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_double)]),
         "ringsim_debug_tree": (res, [i, i, ctypes.POINTER(ctypes.c_int)]),
         "ringsim_debug_tree_model": (res, [i, i, sz, ctypes.POINTER(ctypes.c_double)]),
+        "ringsim_allreduce_noalloc": (res, [i, i, _c_ptrs, _c_ptrs, sz, i, i, vp]),
     }
     for name, (rt, args) in sig.items():
         f = getattr(L, name)
@@ -294,6 +296,18 @@ def allreduce(comm: Comm, sendbufs, recvbufs, count: int | None = None, op: str 
     s, r, dt = _marshal(comm, sendbufs, recvbufs, dtype, n, n)
     o = OPS[op] if isinstance(op, str) else int(op)
     _check(lib().ringsim_allreduce(comm, s, r, n, dt, o, _stream(stream)), "ringsim_allreduce")
+
+
+def allreduce_noalloc(nranks: int, nchannels: int, sendbufs, recvbufs, count: int | None = None,
+                      op: str | int = "sum", stream=None, dtype=None) -> None:
+    """The allocation-free all-reduce: the ring all-reduce of a communicator
+    with ``nranks`` ranks and ``nchannels`` channels, run on the library's
+    per-GPU scratch array instead of a communicator's memory."""
+    n = _numel(sendbufs[0]) if count is None else count
+    s, r, dt = _marshal(Comm(0, nranks), sendbufs, recvbufs, dtype, n, n)
+    o = OPS[op] if isinstance(op, str) else int(op)
+    _check(lib().ringsim_allreduce_noalloc(nranks, nchannels, s, r, n, dt, o, _stream(stream)),
+           "ringsim_allreduce_noalloc")
 
 
 def reduce_scatter(comm: Comm, sendbufs, recvbufs, recvcount: int | None = None, op: str | int = "sum",

@@ -505,6 +505,83 @@ void free_comm_memory(ringsim_comm* c) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Allocation-free all-reduce: the bulk ring kernel on a file-scope scratch
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Geometry of the allocation-free call: at most kNaMaxPipes ring pipelines
+// (ranks x channels x workgroups per channel), 8 FIFO slots of 32 KiB each,
+// and a stage that moves at most 4 slot steps before the next stage runs
+// (step groups), so one stage never fills more than half of a FIFO whatever
+// the chunk size. The partition (channels, loops, chunks) is the
+// communicator's, so results equal ringsim_allreduce's bit for bit.
+constexpr int kNaMaxPipes = 128;
+constexpr int kNaSlots = 8;
+constexpr int kNaSlotBytes = kDefaultSlotBytes;
+constexpr int kNaGroupSteps = kNaSlots / 2;
+constexpr size_t kNaCtrBytes = (size_t)kNaMaxPipes * sizeof(FifoCtr);  // 32 KiB
+constexpr size_t kNaWordBytes = 256;  // device abort word, error word, a never-set abort word
+constexpr size_t kNaFifoBytes = (size_t)kNaMaxPipes * kNaSlots * kNaSlotBytes;  // 32 MiB
+constexpr size_t kNaScratchBytes = kNaCtrBytes + kNaWordBytes + kNaFifoBytes;
+constexpr int kNaMaxDevices = 64;
+
+}  // namespace
+
+// One copy per GPU, held until the process ends: counters, then the error
+// words, then the FIFO slots. Host code never passes this name to a kernel
+// (on the host it is only a stand-in for the symbol); it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[kNaScratchBytes];
+
+namespace {
+
+// Zeroes the counters and error words of the scratch before every call: a
+// call that gave up leaves them behind, and every call starts its counters
+// at zero. A kernel rather than a memset, so that calls can be captured.
+__global__ void __launch_bounds__(kThreads) noalloc_clear(uint4* p, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct NaDevice {
+  char* base;  // device address of `scratch` on this GPU
+  int cus;
+  int per_cu;  // resident bulk workgroups per compute unit
+  int clock_khz;
+};
+
+std::mutex g_na_mu;
+NaDevice g_na[kNaMaxDevices];
+bool g_na_ready[kNaMaxDevices];
+
+// Set-up on a device's first call, with that device current: the device
+// address of its copy of the scratch array, and what the launch needs of it.
+const NaDevice* na_device(int dev) {
+  if (dev < 0 || dev >= kNaMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_na_mu);
+  if (g_na_ready[dev]) return &g_na[dev];
+  NaDevice d{};
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  d.base = static_cast<char*>(ptr);
+  if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&d.clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || d.cus <= 0 ||
+      d.clock_khz <= 0)
+    return nullptr;
+  d.per_cu = bulk_blocks_per_cu(2 * (size_t)kNaSlotBytes);
+  if (d.per_cu <= 0) return nullptr;
+  g_na[dev] = d;
+  g_na_ready[dev] = true;
+  return &g_na[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 ringsim_result_t ringsim_config_default(ringsim_config_t* cfg) {
@@ -933,5 +1010,92 @@ ringsim_result_t ringsim_debug_plan(int coll, size_t count, int nranks, int ncha
   return RINGSIM_SUCCESS;
 }
 
+
+ringsim_result_t ringsim_allreduce_noalloc(int nranks, int nchannels, const void* const* sendbufs,
+                                           void* const* recvbufs, size_t count, int dtype, int op,
+                                           ringsim_stream_t stream) {
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS)
+    return RINGSIM_INVALID_ARGUMENT;
+  if ((int64_t)nranks * nchannels > kNaMaxPipes) {
+    RS_LOG(kLogWarn, "allreduce_noalloc: %d ranks x %d channels exceeds the scratch limit of %d ring pipelines",
+           nranks, nchannels, kNaMaxPipes);
+    return RINGSIM_INVALID_ARGUMENT;
+  }
+  if (!valid_dtype(dtype) || !valid_op(op)) return RINGSIM_INVALID_ARGUMENT;
+  const int esize = dtype_size(dtype);
+  if (count > (size_t)(INT64_MAX / 16) / (size_t)nranks / (size_t)esize) return RINGSIM_INVALID_ARGUMENT;
+  ringsim_config_t cfg;
+  ringsim_config_default(&cfg);
+  if (cfg.chunk_bytes == 0 || cfg.chunk_bytes % 16 || cfg.chunk_bytes > ((size_t)1 << 30) || cfg.timeout_ms <= 0)
+    return RINGSIM_INVALID_ARGUMENT;
+  if (count == 0) return RINGSIM_SUCCESS;
+  if (!sendbufs || !recvbufs) return RINGSIM_INVALID_ARGUMENT;
+  bool vec = true;
+  for (int r = 0; r < nranks; ++r) {
+    const uintptr_t s = (uintptr_t)sendbufs[r], d = (uintptr_t)recvbufs[r];
+    if (!s || !d || (s % esize) || (d % esize)) return RINGSIM_INVALID_ARGUMENT;
+    if ((s | d) & 15u) vec = false;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  const NaDevice* d = na_device(dev);
+  if (!d) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nranks == 1) {
+    if (sendbufs[0] == recvbufs[0]) return RINGSIM_SUCCESS;
+    CopyArgs ca;
+    std::memset(&ca, 0, sizeof(ca));
+    ca.src[0] = static_cast<const char*>(sendbufs[0]);
+    ca.dst[0] = static_cast<char*>(recvbufs[0]);
+    ca.block_bytes = (int64_t)count * esize;
+    ca.nranks = 1;
+    ca.vec_ok = vec;
+    return launch_copy(ca, s) == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR;
+  }
+  // Workgroups per channel: two per compute unit, within the scratch's
+  // pipelines and what the device holds at once (every workgroup spins on
+  // its neighbours).
+  const int64_t nc = (int64_t)nranks * nchannels;
+  const int64_t resident = (int64_t)d->per_cu * d->cus;
+  int wpc = (int)std::max<int64_t>(
+      1, std::min<int64_t>({(int64_t)RINGSIM_MAX_WORKGROUPS_PER_CHANNEL, 2 * (int64_t)d->cus / nc, kNaMaxPipes / nc}));
+  while (wpc > 1 && nc * wpc > resident) --wpc;
+  if (nc * wpc > resident) return RINGSIM_INVALID_USAGE;
+
+  RingArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.send[r] = static_cast<const char*>(sendbufs[r]);
+    a.recv[r] = static_cast<char*>(recvbufs[r]);
+  }
+  a.count = (int64_t)count;
+  a.chunk = (int64_t)cfg.chunk_bytes / esize;
+  a.nranks = nranks;
+  a.nchannels = nchannels;
+  a.wpc = wpc;
+  a.pipe_stride = nchannels * wpc;
+  a.pipe_mul = wpc;
+  a.fifo_stride = nchannels * wpc;
+  a.fifo_mul = wpc;
+  a.nslots = kNaSlots;
+  a.slot_bytes = kNaSlotBytes;
+  a.vec_ok = vec;
+  a.ctr = reinterpret_cast<FifoCtr*>(d->base);
+  uint32_t* words = reinterpret_cast<uint32_t*>(d->base + kNaCtrBytes);
+  a.dev_abort = words;
+  a.host_err = words + 1;
+  a.host_abort = words + 2;  // nothing sets it: this call has no abort
+  a.fifo = d->base + kNaCtrBytes + kNaWordBytes;
+  a.timeout_ticks = (uint64_t)cfg.timeout_ms * (uint64_t)d->clock_khz;
+  a.skip_rank = -1;
+  a.lds_stage = 1;
+  a.group = kNaGroupSteps;
+  const int nclear = (int)((kNaCtrBytes + kNaWordBytes) / 16);
+  hipLaunchKernelGGL(noalloc_clear, dim3((nclear + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                     reinterpret_cast<uint4*>(d->base), nclear);
+  if (hipGetLastError() != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  if (launch_ring_bulk(a, kAllReduce, dtype, op, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  return RINGSIM_SUCCESS;
+}
 
 }  // extern "C"
