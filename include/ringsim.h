@@ -28,8 +28,8 @@
  *     be issued from one host thread and must be ordered on the device (one
  *     stream, or streams ordered by events): the FIFOs are shared state.
  *   - Calls may be captured into a HIP graph (stream capture): a call
- *     enqueues kernel launches only (no memset, copy, event or
- *     synchronization), and every kernel reads where its FIFOs stand from
+ *     made while its stream is capturing enqueues kernel launches only (no
+ *     memset, copy, event or synchronization), and every kernel reads where its FIFOs stand from
  *     the communicator's persistent step counters when it starts, so graph
  *     launches and direct calls may follow one another in any order as long
  *     as they are ordered on the device. What ringsim_comm_query reports
@@ -192,6 +192,8 @@ typedef struct {
   int line_max_workgroups_per_channel; /* most workgroups per channel a FLAG/WIDE launch may take */
   int last_workgroups_per_channel;     /* workgroups per channel of the latest ring call, 0 if none */
   int last_tree_channels;              /* channels per tree of the latest all-reduce, 0 if it ran the ring */
+  uint64_t line_fifo_resets;           /* times the FLAG/WIDE FIFOs and counters were zeroed (flag span) */
+  uint64_t tree_fifo_resets;           /* the same for the tree FIFOs */
 } ringsim_comm_info_t;
 
 /* Fills *cfg with the defaults ("NCCL" book, ch. 3, s. 3.5: every tunable is
@@ -275,11 +277,13 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
 /* Reports the communicator's asynchronous state ("NCCL" book, ch. 2, s. 2.1:
  * the asyncResult field of ncclComm; s. 2.6: asyncResult becomes success when
  * every channel is done, and ncclCommGetAsyncError reads it): RINGSIM_SUCCESS,
- * RINGSIM_IN_PROGRESS while enqueued work on the stream of the latest call
- * is still running and no error is known, or the error a kernel or
- * ringsim_abort left behind. While that stream is being captured into a
- * graph it is not queried (that would end the capture): only known errors
- * are reported. */
+ * RINGSIM_IN_PROGRESS while the latest call enqueued outside stream capture
+ * has not finished and no error is known, or the error a kernel or
+ * ringsim_abort left behind. Completion is tracked by an event the
+ * communicator owns and records after each such call, never by the
+ * caller's stream, which may have been destroyed since. Calls captured into
+ * a graph record nothing: their launches are not tracked, and only the
+ * errors their kernels leave are reported. */
 ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error);
 
 /* Raises the abort word that every spinning kernel polls ("NCCL" book, ch. 3,
@@ -322,6 +326,27 @@ ringsim_result_t ringsim_debug_tree(int nranks, int rank, int* links);
  * and steps growing with the tree's workgroups per compute unit beyond one.
  * Writes the predicted microseconds. */
 ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t bytes_per_rank, double* us);
+
+/* Host-only bound behind the flag span of the line protocols and the tree.
+ * FLAG and WIDE lines, and the tree's lines, carry the low 32 bits of
+ * (step + 1) as their flag ("NCCL" book, s. 2.4: LL and LL128 put a flag
+ * equal to the step into every line, so the receiver polls the data
+ * itself); a line left from step s would match step s + 2^32, and a zeroed
+ * line step 2^32 - 1. Each communicator therefore counts, per family (ring
+ * lines, tree), an upper bound of the steps any FIFO has moved since its
+ * FIFOs and counters were last zeroed, and zeroes them (a kernel on the
+ * call's stream) before a call that could take a counter past 2^31; a call
+ * whose own bound exceeds 2^31 returns RINGSIM_INVALID_USAGE. Calls captured
+ * into a graph are not counted, and a kernel that starts from a counter past
+ * 2^31 (only graph replays can take it there) leaves RINGSIM_INTERNAL_ERROR
+ * (RINGSIM_DEBUG_FLAG_SPAN=n lowers the bound that triggers the zeroing to n
+ * steps, for tests). Writes to *steps the bound for one call: `algo`
+ * RINGSIM_ALGO_RING with `proto` RINGSIM_PROTO_FLAG or _WIDE and `coll`
+ * RINGSIM_COLL_ALLREDUCE, _REDUCE_SCATTER or _ALL_GATHER (count as
+ * ringsim_debug_plan), or RINGSIM_ALGO_TREE for an all-reduce of `count`
+ * elements per rank. Touches no device. */
+ringsim_result_t ringsim_debug_flag_steps(int coll, int algo, int nranks, int nchannels, size_t chunk_bytes,
+                                         size_t count, int dtype, int proto, uint64_t* steps);
 
 /* Host-only view of the partition used by the kernels ("NCCL" book, ch. 2,
  * s. 2.2: a channel owns count / nChannels of the data; s. 2.3: a loop of

@@ -16,6 +16,7 @@ Functions carry the C names without the ``ringsim_`` prefix:
     debug_plan(coll, count, nranks, nchannels, chunk_bytes, dtype)
     debug_model(coll, nranks, nchannels, bytes_per_rank)
     debug_tree(nranks, rank); debug_tree_model(nranks, tree_channels, bytes_per_rank)
+    debug_flag_steps(coll, algo, nranks, nchannels, chunk_bytes, count, dtype, proto)
 
 ``sendbufs``/``recvbufs`` are lists (one per simulated rank) of CUDA/HIP
 tensors of one dtype, or of raw device addresses (ints; then ``dtype`` and the
@@ -103,6 +104,8 @@ class CommInfo(ctypes.Structure):
         ("line_max_workgroups_per_channel", ctypes.c_int),
         ("last_workgroups_per_channel", ctypes.c_int),
         ("last_tree_channels", ctypes.c_int),
+        ("line_fifo_resets", ctypes.c_uint64),
+        ("tree_fifo_resets", ctypes.c_uint64),
     ]
 
     def as_dict(self) -> dict:
@@ -143,6 +146,7 @@ def lib() -> ctypes.CDLL:
         "ringsim_debug_tree": (res, [i, i, ctypes.POINTER(ctypes.c_int)]),
         "ringsim_debug_tree_model": (res, [i, i, sz, ctypes.POINTER(ctypes.c_double)]),
         "ringsim_allreduce_noalloc": (res, [i, i, _c_ptrs, _c_ptrs, sz, i, i, vp]),
+        "ringsim_debug_flag_steps": (res, [i, i, i, i, sz, sz, i, i, ctypes.POINTER(ctypes.c_uint64)]),
     }
     for name, (rt, args) in sig.items():
         f = getattr(L, name)
@@ -365,6 +369,20 @@ def debug_tree_model(nranks: int, tree_channels: int, bytes_per_rank: int) -> fl
     _check(lib().ringsim_debug_tree_model(nranks, tree_channels, bytes_per_rank, ctypes.byref(us)),
            "ringsim_debug_tree_model")
     return us.value
+
+
+def debug_flag_steps(coll: str | int, algo: str | int, nranks: int, nchannels: int, chunk_bytes: int, count: int,
+                     dtype: str | int, proto: str | int = "flag") -> int:
+    """Upper bound of the steps one FIFO moves in a line (or tree) call, as
+    the flag-span bookkeeping counts it; host-only."""
+    c = COLLS[coll] if isinstance(coll, str) else int(coll)
+    a = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    d = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    p = PROTOS[proto] if isinstance(proto, str) else int(proto)
+    out = ctypes.c_uint64(0)
+    _check(lib().ringsim_debug_flag_steps(c, a, nranks, nchannels, chunk_bytes, count, d, p, ctypes.byref(out)),
+           "ringsim_debug_flag_steps")
+    return out.value
 
 
 def debug_plan(coll: str | int, count: int, nranks: int, nchannels: int, chunk_bytes: int, dtype: str | int):

@@ -1,4 +1,5 @@
-// copy.hip -- all-to-all as a block transpose, and one-rank local copies.
+// copy.hip -- all-to-all as a block transpose, one-rank local copies, and
+// the zero fill that resets FIFOs and counters.
 #include <algorithm>
 
 #include "ringsim_device.h"
@@ -75,6 +76,19 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
   }
 }
 
+
+__global__ void __launch_bounds__(kThreads) zero_kernel(u32x4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, p + i);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(kCopyWorkgroups, div_up(n, kThreads)));
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, static_cast<u32x4*>(p), n);
+  return hipGetLastError();
+}
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
   const int nblk = a.transpose ? a.nranks * a.nranks : a.nranks;

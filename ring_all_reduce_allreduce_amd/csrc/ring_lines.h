@@ -8,9 +8,12 @@
 // The two line formats, FLAG and WIDE, are described in line_format.h.
 //
 // Lines carry a flag equal to the low 32 bits of (step + 1), taken from the
-// same monotonic step counters as the bulk protocol, so a line left over from
-// an earlier step (of either format) never matches: that would take 2^32
-// steps on one FIFO. Both formats share one FIFO array per workgroup count.
+// monotonic step counters of the line protocols (the bulk protocol has
+// counters of its own), so a line left over from an earlier step (of either
+// format) never matches while a counter stays below 2^32 - 1: the host zeroes
+// the line FIFOs and their counters before its calls could take a counter
+// past that (kFlagSpanGuard). Both formats share one FIFO array per
+// workgroup count.
 //
 // Workgroups per channel: a launch may split every unit over wpc = 1, 2, 4 or
 // 8 workgroups per (rank, channel), each a pipeline of its own (own part of
@@ -56,6 +59,7 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   if (threadIdx.x == 0) {
     s_base[0] = ld_relaxed(&p.in_ctr->head);
     s_base[1] = ld_relaxed(&p.out_ctr->tail);
+    if (s_base[0] > kFlagSpanGuard || s_base[1] > kFlagSpanGuard) raise_error(wait_ctx(a), kErrFlagSpan);
   }
   __syncthreads();
   const uint64_t in_base = uniform64(s_base[0]);

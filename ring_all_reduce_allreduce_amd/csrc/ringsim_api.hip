@@ -100,8 +100,18 @@ struct ringsim_comm {
   size_t fifo_bytes;
   char* flag_fifo;
   size_t flag_fifo_bytes;
-  FifoCtr* ctr;
+  FifoCtr* ctr;       // line protocols: [rank][channel * pipe_mul + part]
   size_t ctr_bytes;
+  FifoCtr* bulk_ctr;  // bulk protocol: [rank][channel * wpc + part]
+  size_t bulk_ctr_bytes;
+  // Flag span (kFlagSpanGuard): upper bounds of the steps any line or tree
+  // FIFO has moved since its FIFOs and counters were last zeroed, the bound
+  // that triggers the next zeroing, and how often it happened.
+  uint64_t line_span;
+  uint64_t tree_span;
+  uint64_t span_limit;
+  uint64_t line_resets;
+  uint64_t tree_resets;
   uint32_t* dev_abort;
   uint32_t* host_words;      // [0] abort request, [1] kernel error (host view)
   uint32_t* host_words_dev;  // the same words as the device sees them
@@ -119,8 +129,11 @@ struct ringsim_comm {
   FifoCtr* tree_ctr;
   size_t tree_ctr_bytes;
   ringsim_result_t sticky;
-  hipStream_t last_stream;
-  bool has_last_stream;
+  // Recorded on the call's stream after every call enqueued outside stream
+  // capture: completion is tracked without keeping the caller's stream,
+  // which may be destroyed before the communicator is queried.
+  hipEvent_t done_event;
+  bool event_recorded;
   uint64_t end_magic;
 };
 
@@ -150,6 +163,9 @@ ringsim_result_t poll_async(ringsim_comm* c) {
   } else if (kerr == kErrTimeout) {
     c->sticky = RINGSIM_INTERNAL_ERROR;
     RS_LOG(kLogWarn, "a ring kernel gave up waiting for a peer (timeout %d ms)", c->timeout_ms);
+  } else if (kerr == kErrFlagSpan) {
+    c->sticky = RINGSIM_INTERNAL_ERROR;
+    RS_LOG(kLogWarn, "a line or tree kernel started past the flag span (calls replayed from graphs, untracked)");
   }
   return c->sticky;
 }
@@ -220,6 +236,9 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int li
     a->group = kLineGroupSteps;
   } else {
     a->wpc = c->wpc;
+    a->ctr = c->bulk_ctr;
+    a->pipe_stride = c->nchannels * c->wpc;
+    a->pipe_mul = c->wpc;
     a->fifo = c->fifo;
     a->fifo_stride = c->nchannels * c->wpc;
     a->fifo_mul = c->wpc;
@@ -398,6 +417,59 @@ bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t count) {
   return tree_plan(c, count * (size_t)dtype_size(dtype), dtype_size(dtype)).us < pick_proto(c, kAllReduce, count, dtype).us;
 }
 
+// Flag span bookkeeping. An upper bound on the steps any one FIFO of a ring
+// line launch moves ("NCCL" book, s. 2.3: a loop of N chunks, 2(N-1) sending
+// stages for the all-reduce, N-1 for reduce-scatter and all-gather): loop l
+// hands each stage a unit of at most cur_l elements (the loop's chunk; its
+// workgroup parts are smaller still), moved in ceil(unit / slice) steps, and
+// the chunks of all loops of the longest channel L0 add up to at most
+// L0 / N + A (all-reduce) or L0.
+uint64_t line_steps_bound(int mode, int64_t count, int nranks, int nchannels, int64_t chunk, int esize,
+                          int64_t payload_bytes) {
+  const int64_t A = 16 / esize;
+  const int64_t slice = (int64_t)(kFlagSlotBytes / 16) * payload_bytes / esize;
+  const int64_t L0 = std::min<int64_t>(count, channel_span(count, nchannels, A));
+  if (L0 <= 0) return 0;
+  const bool ar = mode == kAllReduce;
+  const int64_t loops = div_up(L0, ar ? (int64_t)nranks * chunk : chunk);
+  const int64_t units = ar ? L0 / nranks + A : L0;
+  const int64_t sends = ar ? 2 * (int64_t)(nranks - 1) : (int64_t)(nranks - 1);
+  return (uint64_t)(sends * (div_up(units, slice) + loops));
+}
+
+// The same for the double tree: a FIFO carries one tree channel, at most the
+// tree's half of the buffer, one WIDE line per thread and step.
+uint64_t tree_steps_bound(int64_t count, int esize) {
+  const int64_t A = 16 / esize;
+  const int64_t half = align_up(div_up(count, 2), A);
+  return (uint64_t)(div_up(half * esize, (int64_t)kThreads * (esize == 8 ? 8 : 12)) + 1);
+}
+
+// Before a line or tree launch of `bound` steps per FIFO: zero that family's
+// FIFOs and counters first if the steps since the last zeroing could take a
+// counter past the span (then flags restart at 1 over all-zero lines). Not
+// while the stream is captured: a zeroing kernel in a graph would run at
+// every replay; replayed launches are not counted here, and a kernel that
+// starts past kFlagSpanGuard reports it.
+ringsim_result_t guard_span(ringsim_comm* c, bool tree, uint64_t bound, bool capturing, hipStream_t s) {
+  if (bound > kFlagSpanGuard) {
+    RS_LOG(kLogWarn, "a line or tree call of %llu steps per FIFO exceeds the flag span", (unsigned long long)bound);
+    return RINGSIM_INVALID_USAGE;
+  }
+  if (capturing) return RINGSIM_SUCCESS;
+  uint64_t& span = tree ? c->tree_span : c->line_span;
+  if (span + bound > c->span_limit) {
+    hipError_t e = tree ? launch_zero(c->tree_fifo, c->tree_fifo_bytes, s) : launch_zero(c->flag_fifo, c->flag_fifo_bytes, s);
+    if (e == hipSuccess) e = tree ? launch_zero(c->tree_ctr, c->tree_ctr_bytes, s) : launch_zero(c->ctr, c->ctr_bytes, s);
+    if (e != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+    span = 0;
+    ++(tree ? c->tree_resets : c->line_resets);
+    RS_LOG(kLogInfo, "comm %p: %s FIFOs zeroed (flag span)", (void*)c, tree ? "tree" : "line");
+  }
+  span += bound;
+  return RINGSIM_SUCCESS;
+}
+
 ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const* rb, size_t count, int dtype,
                              int op, bool vec, hipStream_t s) {
   TreeArgs a;
@@ -431,6 +503,30 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   return RINGSIM_SUCCESS;
 }
 
+// Is `s` being captured into a graph? (A stream the runtime cannot tell
+// about is taken as not captured.)
+bool is_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cap != hipStreamCaptureStatusNone;
+}
+
+// After a call's kernels are enqueued: record the completion event, unless
+// the stream is being captured (a graph's launches are not tracked; an event
+// record would also become a node of the graph).
+ringsim_result_t note_enqueued(ringsim_comm* c, hipStream_t s, bool capturing, ringsim_result_t res) {
+  if (res != RINGSIM_SUCCESS || capturing) return res;
+  if (hipEventRecord(c->done_event, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
+  c->event_recorded = true;
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
+                                 int dtype, int op, hipStream_t s, bool vec, bool capturing);
+
 ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
                           int dtype, int op, ringsim_stream_t stream) {
   ringsim_result_t res = check_comm(c);
@@ -446,8 +542,14 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   if ((res = check_device(c)) != RINGSIM_SUCCESS) return res;
   hipStream_t s = static_cast<hipStream_t>(stream);
   c->calls++;
-  c->last_stream = s;
-  c->has_last_stream = true;
+  const bool capturing = is_capturing(s);
+  return note_enqueued(c, s, capturing, run_ring_launch(c, mode, sb, rb, count, dtype, op, s, vec, capturing));
+}
+
+ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
+                                 int dtype, int op, hipStream_t s, bool vec, bool capturing) {
+  const int esize = dtype_size(dtype);
+  const int64_t n = c->nranks;
   if (n == 1) {
     // A single rank is a local copy ("NCCL" book, enqueue chapter, taskAppend).
     return launch_local_copy(c, sb, rb, count * esize, s);
@@ -457,7 +559,10 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
                       (c->algo == RINGSIM_ALGO_AUTO && auto_picks_tree(c, dtype, op, count));
     c->last_algo = tree ? RINGSIM_ALGO_TREE : RINGSIM_ALGO_RING;
     c->last_tree_channels = 0;
-    if (tree) return launch_tree(c, sb, rb, count, dtype, op, vec, s);
+    if (tree) {
+      const ringsim_result_t g = guard_span(c, true, tree_steps_bound((int64_t)count, esize), capturing, s);
+      return g != RINGSIM_SUCCESS ? g : launch_tree(c, sb, rb, count, dtype, op, vec, s);
+    }
   }
   RingArgs a;
   fill_common(c, &a, sb, rb);
@@ -475,6 +580,10 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
     e = launch_ring_bulk(a, mode, dtype, op, s);
   } else {
     const int lp = proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag;
+    const int64_t payload = lp == kLineWide && dtype != RINGSIM_INT64 ? 12 : 8;
+    const ringsim_result_t g = guard_span(
+        c, false, line_steps_bound(mode, a.count, a.nranks, a.nchannels, a.chunk, esize, payload), capturing, s);
+    if (g != RINGSIM_SUCCESS) return g;
     c->last_wpc = a.wpc;
     e = pc.plan.mode == kHostLinesHalf  ? launch_ring_lines_half(a, lp, mode, dtype, op, s)
         : pc.plan.mode == kHostLinesOne ? launch_ring_lines_one(a, lp, mode, dtype, op, s)
@@ -491,12 +600,16 @@ void free_comm_memory(ringsim_comm* c) {
   if (c->fifo) (void)hipFree(c->fifo);
   if (c->flag_fifo) (void)hipFree(c->flag_fifo);
   if (c->ctr) (void)hipFree(c->ctr);
+  if (c->bulk_ctr) (void)hipFree(c->bulk_ctr);
+  c->bulk_ctr = nullptr;
   if (c->tree_fifo) (void)hipFree(c->tree_fifo);
   if (c->tree_ctr) (void)hipFree(c->tree_ctr);
   c->tree_fifo = nullptr;
   c->tree_ctr = nullptr;
   if (c->dev_abort) (void)hipFree(c->dev_abort);
   if (c->host_words) (void)hipHostFree(c->host_words);
+  if (c->done_event) (void)hipEventDestroy(c->done_event);
+  c->done_event = nullptr;
   c->fifo = c->flag_fifo = nullptr;
   c->ctr = nullptr;
   c->dev_abort = nullptr;
@@ -709,6 +822,10 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // so that its neighbours' bounded waits expire (failure-path tests).
   c->skip_rank = (int)env_long("RINGSIM_DEBUG_SKIP_RANK", -1);
   c->lds_stage = lds_stage;
+  // Testing knob: a small flag span makes the host zero the line and tree
+  // FIFOs every few calls, so that the reset path runs in tests.
+  c->span_limit = (uint64_t)std::max<long>(1, env_long("RINGSIM_DEBUG_FLAG_SPAN", (long)kFlagSpanGuard));
+  if (c->span_limit > kFlagSpanGuard) c->span_limit = kFlagSpanGuard;
   c->timeout_ticks = (uint64_t)cfg.timeout_ms * (uint64_t)clock_khz;
   c->compute_units = cus;
   c->blocks_per_cu = per_cu;
@@ -728,15 +845,18 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->fifo_bytes = (size_t)(nc * wpc) * nslots * cfg.slot_bytes;
   c->flag_fifo_bytes = (size_t)nc * line_fifo_per_nc;
   c->ctr_bytes = (size_t)(nc * c->pipe_mul) * sizeof(FifoCtr);
+  c->bulk_ctr_bytes = (size_t)(nc * wpc) * sizeof(FifoCtr);
   const size_t tree_fifos = (size_t)2 * tree_channels * nranks * 2;
   c->tree_fifo_bytes = tree_fifos * kTreeSlots * kTreeSlotBytes;
   c->tree_ctr_bytes = tree_fifos * sizeof(FifoCtr);
   bool ok = hipMalloc((void**)&c->fifo, c->fifo_bytes) == hipSuccess &&
             hipMalloc((void**)&c->flag_fifo, c->flag_fifo_bytes) == hipSuccess &&
             hipMalloc((void**)&c->ctr, c->ctr_bytes) == hipSuccess &&
+            hipMalloc((void**)&c->bulk_ctr, c->bulk_ctr_bytes) == hipSuccess &&
             hipMalloc((void**)&c->dev_abort, 256) == hipSuccess &&
             hipHostMalloc((void**)&c->host_words, 256, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   if (ok) ok = hipHostGetDevicePointer((void**)&c->host_words_dev, c->host_words, 0) == hipSuccess;
+  if (ok) ok = hipEventCreateWithFlags(&c->done_event, hipEventDisableTiming) == hipSuccess;
   if (ok && tree_fifos) {
     ok = hipMalloc((void**)&c->tree_fifo, c->tree_fifo_bytes) == hipSuccess &&
          hipMalloc((void**)&c->tree_ctr, c->tree_ctr_bytes) == hipSuccess &&
@@ -746,6 +866,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   // Flags of the flag-packed FIFO start at zero, a value no step ever uses.
   if (ok) ok = hipMemset(c->flag_fifo, 0, c->flag_fifo_bytes) == hipSuccess &&
                hipMemset(c->ctr, 0, c->ctr_bytes) == hipSuccess &&
+               hipMemset(c->bulk_ctr, 0, c->bulk_ctr_bytes) == hipSuccess &&
                hipMemset(c->dev_abort, 0, 256) == hipSuccess &&
                hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
@@ -816,6 +937,8 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
   info->line_max_workgroups_per_channel = comm->line_wpc_max;
   info->last_workgroups_per_channel = comm->last_wpc;
   info->last_tree_channels = comm->last_tree_channels;
+  info->line_fifo_resets = comm->line_resets;
+  info->tree_fifo_resets = comm->tree_resets;
   return RINGSIM_SUCCESS;
 }
 
@@ -851,8 +974,6 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
   if ((res = check_device(comm)) != RINGSIM_SUCCESS) return res;
   hipStream_t s = static_cast<hipStream_t>(stream);
   comm->calls++;
-  comm->last_stream = s;
-  comm->has_last_stream = true;
   CopyArgs ca;
   std::memset(&ca, 0, sizeof(ca));
   for (int r = 0; r < n; ++r) {
@@ -863,8 +984,8 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
   ca.nranks = (int)n;
   ca.transpose = 1;
   ca.vec_ok = vec && (ca.block_bytes % 16 == 0);
-  if (launch_copy(ca, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
-  return RINGSIM_SUCCESS;
+  return note_enqueued(comm, s, is_capturing(s),
+                       launch_copy(ca, s) == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR);
 }
 
 ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error) {
@@ -872,16 +993,10 @@ ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* 
   if (res != RINGSIM_SUCCESS) return res;
   if (!async_error) return RINGSIM_INVALID_ARGUMENT;
   ringsim_result_t st = poll_async(comm);
-  // A stream that is being captured into a graph must not be queried (that
-  // would end the capture); its calls have not run yet, and only the error
-  // words are reported.
-  bool query = comm->has_last_stream;
-  if (query) {
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    query = hipStreamIsCapturing(comm->last_stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone;
-  }
-  if (st == RINGSIM_SUCCESS && query) {
-    const hipError_t q = hipStreamQuery(comm->last_stream);
+  // Completion of the latest call enqueued outside capture, through the
+  // communicator's own event (never the caller's stream).
+  if (st == RINGSIM_SUCCESS && comm->event_recorded) {
+    const hipError_t q = hipEventQuery(comm->done_event);
     if (q == hipErrorNotReady) {
       st = RINGSIM_IN_PROGRESS;
     } else if (q != hipSuccess) {
@@ -961,6 +1076,26 @@ ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t 
   const int64_t slice = tree_slice_bytes(4);
   *us = tree_model_us(m, nranks, double_tree_depth(nranks), tree_channels, (double)slice, (double)(slice / kThreads),
                       (double)bytes_per_rank, 256);
+  return RINGSIM_SUCCESS;
+}
+
+ringsim_result_t ringsim_debug_flag_steps(int coll, int algo, int nranks, int nchannels, size_t chunk_bytes,
+                                         size_t count, int dtype, int proto, uint64_t* steps) {
+  if (!steps || !valid_dtype(dtype)) return RINGSIM_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RINGSIM_MAX_RANKS || nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS)
+    return RINGSIM_INVALID_ARGUMENT;
+  if (chunk_bytes == 0 || chunk_bytes % 16 || count > ((size_t)1 << 40)) return RINGSIM_INVALID_ARGUMENT;
+  if (coll < RINGSIM_COLL_ALLREDUCE || coll > RINGSIM_COLL_ALL_GATHER) return RINGSIM_INVALID_ARGUMENT;
+  const int esize = dtype_size(dtype);
+  if (algo == RINGSIM_ALGO_TREE) {
+    if (coll != RINGSIM_COLL_ALLREDUCE) return RINGSIM_INVALID_ARGUMENT;
+    *steps = tree_steps_bound((int64_t)count, esize);
+    return RINGSIM_SUCCESS;
+  }
+  if (algo != RINGSIM_ALGO_RING || (proto != RINGSIM_PROTO_FLAG && proto != RINGSIM_PROTO_WIDE))
+    return RINGSIM_INVALID_ARGUMENT;
+  const int64_t payload = proto == RINGSIM_PROTO_WIDE && dtype != RINGSIM_INT64 ? 12 : 8;
+  *steps = line_steps_bound(coll, (int64_t)count, nranks, nchannels, (int64_t)chunk_bytes / esize, esize, payload);
   return RINGSIM_SUCCESS;
 }
 

@@ -46,7 +46,16 @@ static_assert(sizeof(FifoCtr) == 256, "FifoCtr layout");
 enum Mode : int { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 
 // Error codes a kernel leaves in the host-visible error word.
-enum KernelError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrAborted = 2 };
+enum KernelError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrAborted = 2, kErrFlagSpan = 3 };
+
+// Flag span of the line and tree FIFOs. Their flags are the low 32 bits of
+// (step + 1), so a line left from step s would match step s + 2^32, and a
+// zeroed line matches step 2^32 - 1. The host zeroes a communicator's line
+// (or tree) FIFOs and counters before any of its calls could take a counter
+// past kFlagSpanGuard + the call's steps (< 2^32 - 1); a kernel that starts
+// from a counter above kFlagSpanGuard (only launches the host does not see,
+// graph replays, can get there) records kErrFlagSpan.
+constexpr uint64_t kFlagSpanGuard = 1ull << 31;
 
 struct RingArgs {
   const char* send[RINGSIM_MAX_RANKS];
@@ -114,6 +123,10 @@ struct CopyArgs {
   int transpose;        // 1: all-to-all; 0: rank r copies src[r] -> dst[r]
   int vec_ok;
 };
+
+// Zeroes `bytes` (a multiple of 16) at 16-byte aligned device memory p with a
+// kernel (no memset node, so that it can be captured) (copy.hip).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // Kernel launchers (ring_bulk.hip, ring_lines_half.hip, ring_lines_one.hip,
 // ring_lines_multi.hip, tree.hip, copy.hip).

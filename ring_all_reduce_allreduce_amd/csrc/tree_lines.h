@@ -155,6 +155,7 @@ __global__ void __launch_bounds__(kThreads) tree_line_kernel(TreeArgs a) {
     for (int j = 0; j < 2; ++j) {
       s_base[j] = j < nin ? ld_relaxed(&in_ctr[j]->head) : 0;
       s_base[2 + j] = j < nout ? ld_relaxed(&out_ctr[j]->tail) : 0;
+      if (s_base[j] > kFlagSpanGuard || s_base[2 + j] > kFlagSpanGuard) raise_error(wait_ctx(a), kErrFlagSpan);
     }
   }
   __syncthreads();

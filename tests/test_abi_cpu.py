@@ -275,3 +275,59 @@ def test_every_export_cites_the_page_that_defines_it():
             assert "cannot allocate" in comment, name
             continue
         assert any(p in comment for p in PAGE_MARKERS), f"{name}: no page cited in {comment!r}"
+
+
+def _split_part(n, parts, w, align):
+    sub = -(-(-(-n // parts)) // align) * align
+    lo = min(w * sub, n)
+    return min(lo + sub, n) - lo
+
+
+def _exact_line_steps(coll, nranks, nchannels, chunk_bytes, count, dtype, payload, wpc):
+    """Steps of the busiest FIFO of a ring line launch, walked from the
+    library's partition: each sending stage moves its workgroup's part of the
+    stage's unit in ceil(part / slice) steps."""
+    esize = rs.ELEM_SIZE[dtype]
+    align = 16 // esize
+    slice_elems = 1024 * payload // esize
+    rows = rs.debug_plan(coll, count, nranks, nchannels, chunk_bytes, dtype)
+    loops = {}
+    for ch, lp, k, lo, hi in rows:
+        loops.setdefault((ch, lp), {})[k] = hi - lo
+    best = 0
+    sends = range(2 * nranks - 2) if coll == "allreduce" else range(nranks - 1)
+    for ch in range(nchannels):
+        for w in range(wpc):
+            for r in range(nranks):
+                steps = 0
+                for (c2, lp), chunks in loops.items():
+                    if c2 != ch:
+                        continue
+                    for j in sends:
+                        m = chunks[(r + nranks - 1 - j) % nranks] if coll == "allreduce" else chunks[-1]
+                        part = _split_part(m, wpc, w, align)
+                        steps += -(-part // slice_elems)
+                best = max(best, steps)
+    return best
+
+
+@pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
+def test_flag_step_bound_covers_every_fifo(L, coll):
+    """The flag-span bookkeeping's per-call bound is never below the steps the
+    busiest FIFO of the launch really moves (any workgroup split), nor far
+    above it; the tree's bound covers its half of the buffer in 3 KiB (int64:
+    2 KiB) steps."""
+    cases = [(4, 1, 4096, 3, "float32"), (16, 16, 524288, 1 << 20, "int32"), (8, 8, 524288, 5_000_003, "bfloat16"),
+             (3, 2, 65536, 100_003, "int64"), (16, 1, 524288, 1 << 22, "float32"), (2, 4, 16, 999, "int32")]
+    for n, nch, chunk, count, dtype in cases:
+        for proto, payload in (("flag", 8), ("wide", 8 if dtype == "int64" else 12)):
+            bound = rs.debug_flag_steps(coll, "ring", n, nch, chunk, count, dtype, proto)
+            exact = max(_exact_line_steps(coll, n, nch, chunk, count, dtype, payload, w) for w in (1, 2, 4, 8))
+            assert exact <= bound, (coll, n, nch, chunk, count, dtype, proto, exact, bound)
+            assert bound <= 4 * exact + 4 * n + 64, (coll, n, nch, chunk, count, dtype, proto, exact, bound)
+    if coll == "allreduce":
+        for count, dtype in ((1, "int32"), (1000, "float32"), (1 << 20, "bfloat16"), (777_777, "int64")):
+            esize = rs.ELEM_SIZE[dtype]
+            half = -(-(-(-count // 2)) // (16 // esize)) * (16 // esize)
+            per_step = 256 * (8 if esize == 8 else 12)
+            assert rs.debug_flag_steps("allreduce", "tree", 8, 8, 524288, count, dtype) >= -(-half * esize // per_step)

@@ -105,6 +105,36 @@ def test_missing_rank_times_out_and_poisons_the_comm(proto, monkeypatch):
         rs.comm_destroy(comm)
 
 
+def test_missing_rank_in_the_tree_times_out_then_abort_is_sticky(monkeypatch):
+    """The double-tree kernel's bounded waits: with rank 2's workgroups gone,
+    its parent's and children's polls expire (INTERNAL_ERROR); an abort
+    afterwards leaves the communicator ABORTED for every later call."""
+    import torch
+
+    monkeypatch.setenv("RINGSIM_DEBUG_SKIP_RANK", "2")
+    n, count = 8, 50_000
+    comm = rs.comm_init(n, 2, "auto", algo="tree", timeout_ms=50)
+    monkeypatch.delenv("RINGSIM_DEBUG_SKIP_RANK")
+    try:
+        send = [torch.ones(count, dtype=torch.int32, device="cuda:0") for _ in range(n)]
+        recv = [torch.zeros(count, dtype=torch.int32, device="cuda:0") for _ in range(n)]
+        G.say("tree all-reduce, skip rank 2, timeout 50 ms")
+        t0 = time.perf_counter()
+        rs.allreduce(comm, send, recv)
+        G.sync()
+        dt = time.perf_counter() - t0
+        assert dt < 5.0, dt
+        assert rs.comm_query(comm)["last_algo"] == 2  # the tree ran
+        assert rs.get_async_error(comm) == 3  # INTERNAL_ERROR: a wait expired
+        rs.abort(comm)
+        assert rs.get_async_error(comm) == 8  # ABORTED
+        with pytest.raises(rs.RingsimError) as ei:
+            rs.allreduce(comm, send, recv)
+        assert ei.value.code == 8
+    finally:
+        rs.comm_destroy(comm)
+
+
 def test_abort_stops_a_stalled_collective(monkeypatch):
     import torch
 
@@ -128,6 +158,38 @@ def test_abort_stops_a_stalled_collective(monkeypatch):
         with pytest.raises(rs.RingsimError) as ei:
             rs.allreduce(comm, send, recv)
         assert ei.value.code == 8
+    finally:
+        rs.comm_destroy(comm)
+
+
+@pytest.mark.parametrize("proto,algo", [("flag", "ring"), ("wide", "ring"), ("auto", "tree")])
+def test_flag_span_zeroing_keeps_results(proto, algo, monkeypatch):
+    """With the flag span lowered to 200 steps the communicator
+    zeroes its line (or tree) FIFOs and counters every few calls; calls of
+    mixed sizes before and after each zeroing all match the plain sum."""
+    import torch
+
+    monkeypatch.setenv("RINGSIM_DEBUG_FLAG_SPAN", "200")
+    n = 8
+    comm = rs.comm_init(n, 4, proto, algo=algo)
+    monkeypatch.delenv("RINGSIM_DEBUG_FLAG_SPAN")
+    try:
+        G.say(f"flag span 200 steps, proto {proto}, algo {algo}")
+        for k, count in enumerate([100_000, 7, 262_144, 33_333, 1_000_000, 4096] * 3):
+            xs = [np.random.default_rng(900 + 10 * k + r).integers(-(1 << 20), 1 << 20, count, endpoint=True)
+                  .astype(np.int32) for r in range(n)]
+            send = [G.to_device(x, "int32") for x in xs]
+            recv = [G.empty_like_rank(count, "int32") for _ in range(n)]
+            rs.allreduce(comm, send, recv)
+            G.sync()
+            want = np.sum(np.stack(xs), axis=0, dtype=np.int32)
+            for r in (0, n - 1):
+                assert np.array_equal(G.to_host(recv[r], "int32"), want), (k, count, r)
+        G.check_comm_ok(comm)
+        info = rs.comm_query(comm)
+        assert info["last_algo"] == (2 if algo == "tree" else 1)
+        resets = info["tree_fifo_resets"] if algo == "tree" else info["line_fifo_resets"]
+        assert resets >= 3, info
     finally:
         rs.comm_destroy(comm)
 
