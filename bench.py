@@ -52,8 +52,8 @@ WORKLOADS = {
     "ar8x25bf16": dict(coll="allreduce", nranks=8, count=13_107_200, dtype="bfloat16", nchannels=16,
                        chunk_bytes=524_288, synth_workload=3, op="sum", buckets=40,
                        desc="DDP bucket ring all-reduce sum, 8 simulated ranks x 25 MiB bf16 "
-                            "(13,107,200 elems, N(0,1e-3)), 16 channels, 40 distinct buckets back to back "
-                            "on one stream (one bucket per step)"),
+                            "(13,107,200 elems, N(0,1e-3)), 16 channels, 40 distinct buckets (each drawn on the "
+                            "device with a seed of its own) back to back on one stream (one bucket per step)"),
     "ar16x256i32": dict(coll="allreduce", nranks=16, count=67_108_864, dtype="int32", nchannels=16,
                         chunk_bytes=524_288, synth_workload=4, op="sum",
                         desc="ring all-reduce sum, 16 simulated ranks x 256 MiB int32, 16 channels"),
@@ -134,10 +134,25 @@ def make_inputs(w: dict):
         return synth.rank_inputs(w["synth_workload"], n, w["count"], dtype, "normal", 1.0)
     if w["synth_workload"] == 4:
         return synth.rank_inputs(4, n, w["count"], dtype, "int", lo=-(1 << 20), hi=(1 << 20))
+    if w.get("buckets", 1) > 1:
+        # DDP buckets are drawn on the device (40 x 200 MiB would take minutes
+        # on the host); bucket 0 comes back for the oracle.
+        import torch
+
+        return [t.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bfloat16" else t.cpu().numpy()
+                for t in ddp_bucket(w, 0)]
     xs = synth.workload_inputs(w["synth_workload"])
     assert xs[0].shape[0] == w["count"] and len(xs) == n
     _ = np
     return xs
+
+
+def ddp_bucket(w: dict, b: int):
+    """Device buffers of DDP bucket b: N(0, 1e-3) bf16 from torch's seeded
+    device generator, seed = 1,000,000 x workload + 1,000 x bucket + rank."""
+    import synth
+
+    return synth.device_inputs(w["synth_workload"], w["nranks"], w["count"], w["dtype"], "normal", 1e-3, bucket=b)
 
 
 def oracle_call(w: dict, xs):
@@ -295,15 +310,19 @@ def size_sweep(args) -> int:
     import synth
 
     coll = args.sweep_coll
-    n, nch = args.sweep_ranks, args.sweep_channels
-    comm = rs.comm_init(n, nch, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo,
-                        line_workgroups_per_channel=args.line_wpc or None)
+    n = args.sweep_ranks
+    comms = {c: rs.comm_init(n, c, args.proto, workgroups_per_channel=args.wpc or None, algo=args.algo,
+                             line_workgroups_per_channel=args.line_wpc or None)
+             for c in sorted({args.sweep_channels, args.sweep_small_channels or args.sweep_channels})}
     size = 8
     k = 0
     while size < max(args.sweep_min_bytes, 4 if coll == "allreduce" else 4 * n):
         size *= 2
         k += 1
     while size <= args.sweep_max_bytes:
+        # below 64 KiB per rank the small-message channel count
+        nch = (args.sweep_small_channels or args.sweep_channels) if size < 65536 else args.sweep_channels
+        comm = comms[nch]
         total = size // 4                                   # elements per rank of the sized buffer
         part = total if coll == "allreduce" else total // n  # the other buffer of RS / AG
         nin = part if coll == "all_gather" else total
@@ -365,7 +384,8 @@ def size_sweep(args) -> int:
         del send, recv
         size *= 2
         k += 1
-    rs.comm_destroy(comm)
+    for c in comms.values():
+        rs.comm_destroy(c)
     return 0
 
 
@@ -416,6 +436,8 @@ def main() -> int:
     ap.add_argument("--sweep-max-bytes", type=int, default=256 << 20)
     ap.add_argument("--sweep-ranks", type=int, default=16)
     ap.add_argument("--sweep-channels", type=int, default=16)
+    ap.add_argument("--sweep-small-channels", type=int, default=1,
+                    help="channels below 64 KiB per rank (0 = --sweep-channels)")
     ap.add_argument("--sweep-op", default="sum", choices=["sum", "max"])
     ap.add_argument("--sweep-coll", default="allreduce", choices=["allreduce", "reduce_scatter", "all_gather"])
     ap.add_argument("--proto", default="auto", choices=["auto", "bulk", "flag", "wide"])
@@ -458,21 +480,14 @@ def main() -> int:
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
-    send = [upload(x) for x in xs]
     nbuckets = w.get("buckets", 1)
+    send = None if coll == "allreduce" and nbuckets > 1 else [upload(x) for x in xs]
     if coll == "allreduce" and nbuckets > 1:
-        # Distinct buckets back to back: bucket b holds base bucket b mod 5
-        # with its ranks rotated by b // 5 (the seeded inputs of 5 base
-        # buckets, shared read-only), and a receive buffer set of its own.
-        import synth
-
-        base = [send] + [[upload(x) for x in synth.rank_inputs(w["synth_workload"], n, w["count"], dtype, "normal",
-                                                                1e-3, bucket=b)] for b in range(1, 5)]
-        sends, recvs = [], []
-        for b in range(nbuckets):
-            bb, src = synth.ddp_bucket_ranks(b, n)
-            sends.append([base[bb][r] for r in src])
-            recvs.append([torch.empty_like(send[0]) for _ in range(n)])
+        # Distinct buckets back to back, each with seeded inputs of its own
+        # (drawn on the device) and a receive buffer set of its own.
+        sends = [ddp_bucket(w, b) for b in range(nbuckets)]
+        send = sends[0]
+        recvs = [[torch.empty_like(send[0]) for _ in range(n)] for _ in range(nbuckets)]
         per_rank_bytes = w["count"] * esize
         bucket = [0]
 

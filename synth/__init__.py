@@ -15,7 +15,8 @@ Workloads (shapes follow the pages' use cases; no benchmark data is copied):
      [-8, 8] (inclusive) stored as fp32 so every sum is exact.
   2  large AllReduce: 8 ranks x 16,777,216 fp32 (64 MiB) ~ N(0, 1).
   3  DDP gradient bucket: 8 ranks x 13,107,200 bf16 (25 MiB) ~ N(0, 1e-3),
-     40 distinct buckets.
+     40 distinct buckets (bucket b drawn with seed ... + 1,000 b; at full size
+     on the device, see device_inputs).
   4  message-size sweep: 16 ranks, int32 uniform in [-2^20, 2^20] (inclusive).
   5  FSDP / MoE: reduce-scatter of 8 ranks x 67,108,864 bf16 (128 MiB) ~ N(0,1);
      all-to-all of 8 chunks x 512 tokens x 4096 bf16 uniform in [-1, 1).
@@ -151,10 +152,3 @@ def device_inputs(workload: int, nranks: int, n: int, dtype: str, dist: str, sca
         else:
             raise ValueError(dist)
     return out
-
-
-def ddp_bucket_ranks(bucket: int, nranks: int = 8, distinct: int = 5) -> tuple[int, list[int]]:
-    """The 40 DDP buckets reuse ``distinct`` seeded base buckets: bucket b takes
-    base bucket b mod distinct, and rank r holds that base bucket's rank
-    (r + b // distinct) mod nranks. Returns (base bucket, source rank per rank)."""
-    return bucket % distinct, [(r + bucket // distinct) % nranks for r in range(nranks)]

@@ -1,8 +1,10 @@
 """The named workloads at full size on the MI355X, in the launch configuration
-bench.py times. Where the oracle can replay the whole call in seconds it does;
-otherwise the oracle computes sampled elements one by one (the ring fold of
-those elements across ranks) and properties that hold at any size are checked
-on every element (all ranks agree; blocks land where the definition says)."""
+bench.py times, compared with the oracle on every element: whole calls where
+the oracle replays them in seconds, column blocks of all ranks where the
+result does not depend on the fold order (int32 sums and maxima), whole
+blocks for the reduce-scatter (the oracle's reduce to the block's rank);
+properties that hold at any size are checked too (all ranks agree; blocks
+land where the definition says)."""
 import numpy as np
 import pytest
 
@@ -25,19 +27,6 @@ def _device():
     torch.cuda.empty_cache()
 
 
-def _sample_idx(n, k, seed):
-    rng = np.random.default_rng(seed)
-    idx = np.unique(np.concatenate([rng.integers(0, n, k), [0, n - 1], np.arange(min(n, 64))]))
-    return idx
-
-
-def _host_at(t, idx, dtype):
-    import torch
-
-    sel = t.index_select(0, torch.from_numpy(idx).to(t.device))
-    return G.to_host(sel, dtype)
-
-
 def _bits(t):
     import torch
 
@@ -51,38 +40,38 @@ def _all_ranks_equal(recv):
 
 
 def test_workload3_ddp_buckets_back_to_back():
-    """40 bucket all-reduces (8 ranks x 25 MiB bf16, 16 channels) enqueued
-    back to back on one stream, checked after one synchronisation."""
+    """40 distinct bucket all-reduces (8 ranks x 25 MiB bf16, 16 channels,
+    seeded inputs of their own drawn on the device) enqueued back to back on
+    one stream, checked after one synchronisation: every bucket on one rank
+    against the oracle, element by element, and all ranks against each
+    other."""
     import torch
 
     w = synth.WORKLOADS[3]
     n, count, nch = w["nranks"], w["n"], w["nchannels"]
-    base = [synth.rank_inputs(3, n, count, "bfloat16", "normal", 1e-3, bucket=b) for b in range(5)]
-    base_dev = [[G.to_device(x, "bfloat16") for x in bb] for bb in base]
+    sends = [synth.device_inputs(3, n, count, "bfloat16", "normal", 1e-3, bucket=b) for b in range(w["buckets"])]
     comm = rs.comm_init(n, nch, "auto")
     try:
         recvs = []
-        for b in range(w["buckets"]):
-            bb, src = synth.ddp_bucket_ranks(b, n)
-            send = [base_dev[bb][src[r]] for r in range(n)]
+        for b, send in enumerate(sends):
             recv = [torch.empty(count, dtype=torch.bfloat16, device="cuda:0") for _ in range(n)]
-            G.say(f"ddp bucket {b} base {bb} ranks {src}")
             rs.allreduce(comm, send, recv)
             recvs.append(recv)
+        G.say(f"{len(sends)} ddp buckets enqueued")
         G.sync()
         G.check_comm_ok(comm)
         for b in range(w["buckets"]):
             assert _all_ranks_equal(recvs[b]), f"bucket {b}: ranks disagree"
-        for b in (0, 17, 39):
-            bb, src = synth.ddp_bucket_ranks(b, n)
-            xs = [base[bb][src[r]] for r in range(n)]
+            xs = [G.to_host(t, "bfloat16") for t in sends[b]]
             want = oracle.ring_allreduce(xs, "sum", "bfloat16", nchannels=nch)
             got = G.to_host(recvs[b][b % n], "bfloat16")
             mm = G.first_mismatch(got, want[b % n], "bfloat16")
             assert mm is None, f"bucket {b}: {mm}"
-            exact = np.sum(np.stack([oracle.bf16_to_f64(x) for x in xs]), axis=0)
-            g64 = oracle.bf16_to_f64(got)
-            assert np.linalg.norm(g64 - exact) / np.linalg.norm(exact) <= 8e-3
+            if b % 10 == 0:
+                G.say(f"ddp bucket {b} matches the oracle")
+                exact = np.sum(np.stack([oracle.bf16_to_f64(x) for x in xs]), axis=0)
+                g64 = oracle.bf16_to_f64(got)
+                assert np.linalg.norm(g64 - exact) / np.linalg.norm(exact) <= 8e-3
     finally:
         rs.comm_destroy(comm)
 
@@ -90,7 +79,8 @@ def test_workload3_ddp_buckets_back_to_back():
 @pytest.mark.parametrize("choice", ["threshold", "auto"])
 @pytest.mark.parametrize("op", ["sum", "max"])
 def test_workload4_size_sweep(op, choice):
-    """16 ranks, int32 in [-2^20, 2^20], 8 B .. 256 MiB per rank, 16 channels.
+    """16 ranks, int32 in [-2^20, 2^20], 8 B .. 256 MiB per rank; one channel
+    below 64 KiB, 16 channels from 64 KiB up (the sweep's channel choice).
     "threshold": the ring, flag-packed below 64 KiB and bulk above (the
     sweep's own fixed threshold); "auto": whatever algorithm, protocol and
     workgroups the cost model takes (the tree, FLAG, WIDE or BULK). Integer
@@ -98,14 +88,14 @@ def test_workload4_size_sweep(op, choice):
     oracle."""
     import torch
 
-    n, nch = 16, 16
-    if choice == "threshold":
-        comm = rs.comm_init(n, nch, "auto", flag_threshold_bytes=65536, algo="ring")
-    else:
-        comm = rs.comm_init(n, nch, "auto")
+    n = 16
+    cfg = dict(flag_threshold_bytes=65536, algo="ring") if choice == "threshold" else {}
+    comms = {1: rs.comm_init(n, 1, "auto", **cfg), 16: rs.comm_init(n, 16, "auto", **cfg)}
     try:
         for k, size in enumerate(synth.WORKLOADS[4]["sizes_bytes"]):
             count = size // 4
+            nch = 1 if size < 65536 else 16
+            comm = comms[nch]
             want_proto = 2 if size < 65536 else 1
             G.say(f"sweep {choice} op={op} bytes/rank={size}")
             if size <= (4 << 20):
@@ -126,14 +116,21 @@ def test_workload4_size_sweep(op, choice):
                 got = G.to_host(recv[k % n], "int32")
                 assert G.first_mismatch(got, want[0], "int32") is None, f"size {size}"
             else:
-                idx = _sample_idx(count, 50_000, k)
-                cols = [_host_at(t, idx, "int32") for t in send]
-                want = oracle.ring_allreduce(cols, op, "int32", nchannels=1)[0]
-                got = _host_at(recv[k % n], idx, "int32")
-                assert np.array_equal(got, want), f"size {size}"
+                # Every element, in column blocks of all ranks: an int32 sum
+                # (wrapping) or maximum does not depend on the fold order, so
+                # the oracle's ring over one block of columns gives exactly
+                # those columns of the result.
+                blk = 1 << 22
+                for lo in range(0, count, blk):
+                    hi = min(count, lo + blk)
+                    cols = [G.to_host(t[lo:hi], "int32") for t in send]
+                    want = oracle.ring_allreduce(cols, op, "int32", nchannels=1)[0]
+                    got = G.to_host(recv[k % n][lo:hi], "int32")
+                    assert G.first_mismatch(got, want, "int32") is None, f"size {size} columns {lo}:{hi}"
             del send, recv
     finally:
-        rs.comm_destroy(comm)
+        for c in comms.values():
+            rs.comm_destroy(c)
 
 
 def test_workload5_reduce_scatter_then_all_gather():
@@ -154,13 +151,13 @@ def test_workload5_reduce_scatter_then_all_gather():
         rs.all_gather(comm, shard, full)
         G.sync()
         G.check_comm_ok(comm)
-        # reduce-scatter: block b folded b+1, ..., b -- the oracle's reduce to root b
+        # reduce-scatter: block b folded b+1, ..., b -- the oracle's reduce to
+        # root b -- on every element of every shard
         for b in range(n):
-            idx = _sample_idx(rc, 20_000, 100 + b)
-            cols = [_host_at(t, idx + b * rc, "bfloat16") for t in send]
+            cols = [G.to_host(t[b * rc:(b + 1) * rc], "bfloat16") for t in send]
             want = oracle.reduce(cols, b, "sum", "bfloat16")
-            got = _host_at(shard[b], idx, "bfloat16")
-            assert np.array_equal(got, want), f"block {b}"
+            mm = G.first_mismatch(G.to_host(shard[b], "bfloat16"), want, "bfloat16")
+            assert mm is None, f"block {b}: {mm}"
         # all-gather: block b of every output is shard b, on every element
         for r in range(n):
             for b in range(n):
