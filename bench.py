@@ -105,8 +105,9 @@ def bus_factor(coll: str, n: int) -> float:
 
 
 def load_traffic(name: str, src_hash: str):
-    """Counter-measured HBM bytes per launch, if a summary for this workload
-    and this exact kernel source is committed under profiles/."""
+    """Counter-measured bytes per launch between the L2 and the memory side
+    (HBM and Infinity Cache alike), if a summary for this workload and this
+    exact kernel source is committed under profiles/: the record's fields."""
     p = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(p):
         return None
@@ -118,7 +119,7 @@ def load_traffic(name: str, src_hash: str):
                 t[k.strip()] = v.strip()
     if t.get("kernel_source_hash") != src_hash:
         return None
-    return int(t["bytes_per_launch"])
+    return t
 
 
 def make_inputs(w: dict):
@@ -667,9 +668,21 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": int(traffic["bytes_per_launch"]) if traffic else None,
             "bytes_per_launch": bytes_alg,
             "launch_avg_us": round(t_avg * 1e6, 2),
+            # What the bytes are: `achieved` counts the method's algorithmic
+            # bytes, `traffic` the counted bytes between the L2 and the memory
+            # side. Both include the FIFO slots, which the 256 MB Infinity
+            # Cache serves (they are rewritten before HBM sees them), so `frac`
+            # is the byte model's rate against the HBM peak, not HBM's own
+            # utilisation. The user buffers (2N x S, or (N+1) x S for
+            # reduce-scatter / all-gather) must cross HBM: `frac_compulsory`
+            # is that rate, a lower bound of HBM's utilisation.
+            "bytes_counted_at": "L2 to memory side (HBM and Infinity Cache together)",
+            "frac_compulsory": round(compulsory / t_avg / 1e9 / HBM_PEAK_GBS, 4),
+            "dram_request_bytes": int(traffic["dram_request_bytes"]) if traffic and "dram_request_bytes" in traffic
+            else None,
         },
         "cpu_baseline": cpu,
         "extra": {

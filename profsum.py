@@ -2,17 +2,24 @@
 
 Inputs: the kernel_stats.csv of a `--kernel-trace --stats` run, and the
 counter_collection.csv files of separate `--pmc FETCH_SIZE` and
-`--pmc WRITE_SIZE` runs, for the benchmark and for the copy-calibration run
-(`bench.py --copy-calibration`, a copy kernel that reads and writes 1 GiB per
-launch). The counters report KiB per dispatch; each is scaled by
-known bytes / counted bytes of the copy kernel, so that counter quirks of the
-part (e.g. a fetch counter that counts half the bytes) cancel.
+`--pmc WRITE_SIZE` runs (optionally also one `--pmc
+TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum` run), for the
+benchmark and for the copy-calibration run (`bench.py --copy-calibration`, a
+copy kernel that reads and writes 1 GiB per launch). FETCH_SIZE and
+WRITE_SIZE report KiB per dispatch, the DRAM-request counters 32-byte units;
+each is scaled by known bytes / counted bytes of the copy kernel, so that
+counter quirks of the part (e.g. a fetch counter that counts half the bytes)
+cancel. All of them count requests that leave the L2 for the memory side of
+the fabric: the 256 MB Infinity Cache sits there, in front of HBM, and its
+hits are counted the same as HBM accesses.
 
-Writes a markdown report and a `key: value` traffic record that bench.py reads
-to fill roofline.traffic (only while the kernel source hash still matches).
+Writes a markdown report (with this summariser's own command line) and a
+`key: value` traffic record that bench.py reads to fill roofline.traffic
+(only while the kernel source hash still matches).
 
-  python -m ring_all_reduce_allreduce_amd.profsum --name ar8x64 --kernel ring_bulk_kernel \\
+  python profsum.py --name ar8x64 --kernel ring_bulk_kernel \\
       --stats S.csv --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv \\
+      [--dram D.csv --copy-dram CD.csv] \\
       --hash H --algorithmic-bytes B --report profiles/X.md --traffic profiles/traffic_ar8x64.txt \\
       --command "..." [--command "..."]
 """
@@ -20,7 +27,9 @@ from __future__ import annotations
 
 import argparse
 import csv
+import shlex
 import statistics
+import sys
 
 COPY_BYTES = 1 << 30
 
@@ -50,6 +59,9 @@ def main() -> None:
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-fetch", required=True)
     ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--dram", default="", help="counter_collection.csv of the DRAM-request counter run")
+    ap.add_argument("--copy-dram", default="", help="the same run of the copy calibration")
+    ap.add_argument("--out-dir", default="", help="shown as OUT in the report's copy of this command line")
     ap.add_argument("--hash", required=True)
     ap.add_argument("--algorithmic-bytes", type=int, required=True)
     ap.add_argument("--report", required=True)
@@ -75,6 +87,11 @@ def main() -> None:
     for c in a.command:
         lines.append(f"    {c}")
     lines.append("")
+    lines.append("Summarised with (OUT = the directory of the runs above):")
+    lines.append("")
+    argv = [x.replace(a.out_dir, "OUT") if a.out_dir else x for x in sys.argv[1:]]
+    lines.append("    python3 profsum.py " + " ".join(shlex.quote(x) for x in argv))
+    lines.append("")
     lines.append("## Kernel trace statistics")
     lines.append("")
     lines.append("| kernel | calls | avg us | min us | max us | share |")
@@ -85,7 +102,7 @@ def main() -> None:
     target = [r for r in rows if a.kernel in r["Name"]]
     avg_ns = float(target[0]["AverageNs"]) if target else float("nan")
     lines.append("")
-    lines.append("## HBM-side bytes per launch (L2 to fabric)")
+    lines.append("## Bytes per launch between the L2 and the memory side (HBM and Infinity Cache together)")
     lines.append("")
     lines.append(f"- copy calibration: FETCH_SIZE reads {statistics.median(cfetch) / 2**20:.1f} MiB and "
                  f"WRITE_SIZE {statistics.median(cwrite) / 2**20:.1f} MiB for a copy that reads and writes "
@@ -97,6 +114,23 @@ def main() -> None:
                  f"(ratio {traffic / a.algorithmic_bytes:.3f})")
     lines.append(f"- average launch {avg_ns / 1e3:.1f} us -> algorithmic {a.algorithmic_bytes / avg_ns:.0f} GB/s, "
                  f"counted {traffic / avg_ns:.0f} GB/s")
+    dram_b = None
+    if a.dram and a.copy_dram:
+        rd = per_dispatch(a.dram, a.kernel, "TCC_EA0_RDREQ_DRAM_32B_sum")
+        wr = per_dispatch(a.dram, a.kernel, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+        crd = per_dispatch(a.copy_dram, "copy_kernel", "TCC_EA0_RDREQ_DRAM_32B_sum")
+        cwr = per_dispatch(a.copy_dram, "copy_kernel", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+        # per_dispatch scales by 1024 (KiB); these counters are 32-byte units
+        unit = 32.0 / 1024.0
+        rd_s, wr_s = COPY_BYTES / (statistics.median(crd) * unit), COPY_BYTES / (statistics.median(cwr) * unit)
+        rd_b = statistics.median(rd) * unit * rd_s
+        wr_b = statistics.median(wr) * unit * wr_s
+        dram_b = rd_b + wr_b
+        lines.append(f"- requests destined for DRAM (TCC_EA0_RDREQ_DRAM_32B_sum, TCC_EA0_WRREQ_WRITE_DRAM_32B_sum; "
+                     f"copy scale x{rd_s:.4f} / x{wr_s:.4f}): read {rd_b / 2**20:.1f} MiB, write "
+                     f"{wr_b / 2**20:.1f} MiB, {dram_b / 1e9:.4f} GB per launch. These classify requests by "
+                     f"their target (device memory), before the Infinity Cache: they bound HBM bytes from above "
+                     f"like FETCH_SIZE + WRITE_SIZE, and no counter here separates cache hits from HBM")
     lines.append(f"- kernel source hash `{a.hash}`")
     lines.append("")
     with open(a.report, "w") as f:
@@ -105,7 +139,7 @@ def main() -> None:
         f.write(f"workload: {a.name}\nkernel: {a.kernel}\nkernel_source_hash: {a.hash}\n"
                 f"bytes_per_launch: {int(round(traffic))}\nfetch_bytes: {int(round(fetch_b))}\n"
                 f"write_bytes: {int(round(write_b))}\nfetch_scale: {f_scale:.6f}\nwrite_scale: {w_scale:.6f}\n"
-                f"launch_avg_ns: {avg_ns:.0f}\n")
+                f"launch_avg_ns: {avg_ns:.0f}\n" + (f"dram_request_bytes: {int(round(dram_b))}\n" if dram_b else ""))
     print("\n".join(lines))
 
 
