@@ -206,7 +206,11 @@ typedef struct {
  * read once). Environment overrides, read by this call:
  * RINGSIM_CHUNK_BYTES, RINGSIM_WPC, RINGSIM_SLOT_BYTES, RINGSIM_NSLOTS,
  * RINGSIM_TIMEOUT_MS, RINGSIM_FLAG_THRESHOLD, RINGSIM_ALGO, RINGSIM_LINE_WPC;
- * RINGSIM_DEBUG=WARN|INFO logs to stderr. Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
+ * RINGSIM_DEBUG=WARN|INFO logs to stderr. RINGSIM_DEBUG_FIFO=1 (read at comm
+ * init) keeps a (step, bytes) record beside every bulk FIFO slot, written by
+ * its producer and checked by its consumer ("NCCL" book, s. 2.4: the size and
+ * offset each FIFO step carries); a mismatch leaves RINGSIM_INTERNAL_ERROR.
+ * Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
  * the workgroups of simulated rank r return at once, so that the bounded
  * waits of its neighbours expire and the failure path can be exercised. */
 ringsim_result_t ringsim_config_default(ringsim_config_t* cfg);

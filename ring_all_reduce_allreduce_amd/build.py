@@ -14,8 +14,17 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libringsim.so")
-SOURCES = ["ringsim_api.hip", "ring_bulk.hip", "ring_lines_half.hip", "ring_lines_one.hip", "ring_lines_multi.hip",
-           "tree.hip", "copy.hip"]
+# (source, object name, extra defines): the line kernel's instantiation unit
+# is compiled once per line mode.
+SOURCES = [
+    ("ringsim_api.hip", "ringsim_api", []),
+    ("ring_bulk.hip", "ring_bulk", []),
+    ("ring_lines_inst.hip", "ring_lines_half", ["-DRINGSIM_LINE_MODE=kLinesHalf", "-DRINGSIM_LINE_NAME=half"]),
+    ("ring_lines_inst.hip", "ring_lines_one", ["-DRINGSIM_LINE_MODE=kLinesOne", "-DRINGSIM_LINE_NAME=one"]),
+    ("ring_lines_inst.hip", "ring_lines_multi", ["-DRINGSIM_LINE_MODE=kLinesMulti", "-DRINGSIM_LINE_NAME=multi"]),
+    ("tree.hip", "tree", []),
+    ("copy.hip", "copy", []),
+]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
@@ -47,12 +56,12 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="ringsim_build_") as tmp:
         objs = []
         procs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        for src, name, defines in SOURCES:
+            obj = os.path.join(tmp, name + ".o")
+            cmd = [cc, *HIP_FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
             objs.append(obj)
         failed = []
         for src, p in procs:

@@ -210,6 +210,15 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   StepIter<DT, MODE> nx = it;
   if (!nx.done) nx.next();
   const bool lds = a.lds_stage && a.vec_ok;
+  // Debug FIFO integrity records of the slots this workgroup reads and
+  // writes (null unless the communicator was created with RINGSIM_DEBUG_FIFO).
+  FifoEcho* echo_in = nullptr;
+  FifoEcho* echo_out = nullptr;
+  if (a.echo) {
+    const int fpipe = p.c * a.fifo_mul + p.w;
+    echo_in = a.echo + ((int64_t)p.r * a.fifo_stride + fpipe) * a.nslots;
+    echo_out = a.echo + ((int64_t)p.nxt * a.fifo_stride + fpipe) * a.nslots;
+  }
   int buf = 0;
   if (lds && !it.done && it.use_local) {
     stage_to_lds(it.local(), it.ns() / A, lds_stage);
@@ -227,6 +236,13 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
         known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
         stop = known_tail == 0;
       }
+      if (!stop && recv && echo_in) {
+        // Debug: the slot must hold the step and size this step expects.
+        const FifoEcho* e = echo_in + in_slot;
+        const uint64_t step = __hip_atomic_load(&e->step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t bytes = __hip_atomic_load(&e->bytes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (step != in_base + nrecv || bytes != (uint32_t)(it.ns() * (int64_t)sizeof(T))) raise_error(wc, kErrFifoEcho);
+      }
       const uint64_t need_head = out_base + nsent + 1 - nslots;
       if (!stop && send && nsent + 1 > nslots && known_head < need_head) {
         known_head = wait_geq(&p.out_ctr->head, need_head, wc);
@@ -239,6 +255,12 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
     char* fout = send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr;
     move_slice<DT, OP>(ns, fin, it.use_local ? it.local() : nullptr, fout, it.store ? it.out() : nullptr,
                        a.slot_bytes, a.vec_ok, lds && it.use_local ? lds_stage + buf * stage_vecs : nullptr);
+    if (send && echo_out && threadIdx.x == 0) {
+      // Debug: completes with the slot's data, before the tail is published.
+      FifoEcho* e = echo_out + out_slot;
+      __hip_atomic_store(&e->step, out_base + nsent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&e->bytes, (uint32_t)(ns * (int64_t)sizeof(T)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // The next step's own operand streams into the other LDS buffer while
     // this step's stores drain.
     if (lds && !nx.done && nx.use_local) stage_to_lds(nx.local(), nx.ns() / A, lds_stage + (buf ^ 1) * stage_vecs);

@@ -112,6 +112,8 @@ struct ringsim_comm {
   uint64_t span_limit;
   uint64_t line_resets;
   uint64_t tree_resets;
+  FifoEcho* echo;     // bulk debug FIFO records (RINGSIM_DEBUG_FIFO), null = off
+  size_t echo_bytes;
   uint32_t* dev_abort;
   uint32_t* host_words;      // [0] abort request, [1] kernel error (host view)
   uint32_t* host_words_dev;  // the same words as the device sees them
@@ -163,6 +165,9 @@ ringsim_result_t poll_async(ringsim_comm* c) {
   } else if (kerr == kErrTimeout) {
     c->sticky = RINGSIM_INTERNAL_ERROR;
     RS_LOG(kLogWarn, "a ring kernel gave up waiting for a peer (timeout %d ms)", c->timeout_ms);
+  } else if (kerr == kErrFifoEcho) {
+    c->sticky = RINGSIM_INTERNAL_ERROR;
+    RS_LOG(kLogWarn, "a bulk FIFO slot held another step or size than its consumer expected");
   } else if (kerr == kErrFlagSpan) {
     c->sticky = RINGSIM_INTERNAL_ERROR;
     RS_LOG(kLogWarn, "a line or tree kernel started past the flag span (calls replayed from graphs, untracked)");
@@ -246,6 +251,7 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int li
     a->slot_bytes = (int)c->slot_bytes;
     a->lds_stage = c->lds_stage;
     a->group = 0;
+    a->echo = c->echo;
   }
 }
 
@@ -372,7 +378,6 @@ ringsim_result_t launch_local_copy(ringsim_comm* c, const void* const* sb, void*
   ca.block_bytes = (int64_t)bytes;
   ca.nranks = 1;
   ca.transpose = 0;
-  ca.vec_ok = ((((uintptr_t)sb[0]) | ((uintptr_t)rb[0])) & 15u) == 0;
   if (launch_copy(ca, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
   return RINGSIM_SUCCESS;
 }
@@ -602,6 +607,8 @@ void free_comm_memory(ringsim_comm* c) {
   if (c->ctr) (void)hipFree(c->ctr);
   if (c->bulk_ctr) (void)hipFree(c->bulk_ctr);
   c->bulk_ctr = nullptr;
+  if (c->echo) (void)hipFree(c->echo);
+  c->echo = nullptr;
   if (c->tree_fifo) (void)hipFree(c->tree_fifo);
   if (c->tree_ctr) (void)hipFree(c->tree_ctr);
   c->tree_fifo = nullptr;
@@ -846,6 +853,9 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->flag_fifo_bytes = (size_t)nc * line_fifo_per_nc;
   c->ctr_bytes = (size_t)(nc * c->pipe_mul) * sizeof(FifoCtr);
   c->bulk_ctr_bytes = (size_t)(nc * wpc) * sizeof(FifoCtr);
+  // Debug: a (step, bytes) record beside every bulk slot, checked by its
+  // consumer ("NCCL" book, s. 2.4: ncclConnFifo's size and offset per step).
+  c->echo_bytes = env_long("RINGSIM_DEBUG_FIFO", 0) != 0 ? (size_t)(nc * wpc) * nslots * sizeof(FifoEcho) : 0;
   const size_t tree_fifos = (size_t)2 * tree_channels * nranks * 2;
   c->tree_fifo_bytes = tree_fifos * kTreeSlots * kTreeSlotBytes;
   c->tree_ctr_bytes = tree_fifos * sizeof(FifoCtr);
@@ -857,6 +867,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
             hipHostMalloc((void**)&c->host_words, 256, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   if (ok) ok = hipHostGetDevicePointer((void**)&c->host_words_dev, c->host_words, 0) == hipSuccess;
   if (ok) ok = hipEventCreateWithFlags(&c->done_event, hipEventDisableTiming) == hipSuccess;
+  if (ok && c->echo_bytes) ok = hipMalloc((void**)&c->echo, c->echo_bytes) == hipSuccess;
   if (ok && tree_fifos) {
     ok = hipMalloc((void**)&c->tree_fifo, c->tree_fifo_bytes) == hipSuccess &&
          hipMalloc((void**)&c->tree_ctr, c->tree_ctr_bytes) == hipSuccess &&
@@ -983,7 +994,6 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
   ca.block_bytes = (int64_t)count * esize;
   ca.nranks = (int)n;
   ca.transpose = 1;
-  ca.vec_ok = vec && (ca.block_bytes % 16 == 0);
   return note_enqueued(comm, s, is_capturing(s),
                        launch_copy(ca, s) == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR);
 }
@@ -1184,7 +1194,6 @@ ringsim_result_t ringsim_allreduce_noalloc(int nranks, int nchannels, const void
     ca.dst[0] = static_cast<char*>(recvbufs[0]);
     ca.block_bytes = (int64_t)count * esize;
     ca.nranks = 1;
-    ca.vec_ok = vec;
     return launch_copy(ca, s) == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR;
   }
   // Workgroups per channel: two per compute unit, within the scratch's

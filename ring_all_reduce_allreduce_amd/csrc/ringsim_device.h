@@ -257,6 +257,7 @@ __device__ __forceinline__ uint64_t wait_geq(const uint64_t* p, uint64_t target,
 
 struct Pipe {
   int r, c, w, pipe;
+  int nxt;  // the next rank on the ring
   FifoCtr* in_ctr;
   FifoCtr* out_ctr;
   char* in_fifo;
@@ -273,6 +274,7 @@ __device__ __forceinline__ Pipe locate(const RingArgs& a) {
   p.w = pl - p.c * a.wpc;
   p.pipe = p.c * a.pipe_mul + p.w;
   const int nxt = p.r + 1 == a.nranks ? 0 : p.r + 1;
+  p.nxt = nxt;
   p.in_ctr = a.ctr + (int64_t)p.r * a.pipe_stride + p.pipe;
   p.out_ctr = a.ctr + (int64_t)nxt * a.pipe_stride + p.pipe;
   const int fpipe = p.c * a.fifo_mul + p.w;

@@ -46,7 +46,17 @@ static_assert(sizeof(FifoCtr) == 256, "FifoCtr layout");
 enum Mode : int { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 
 // Error codes a kernel leaves in the host-visible error word.
-enum KernelError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrAborted = 2, kErrFlagSpan = 3 };
+enum KernelError : uint32_t { kErrNone = 0, kErrTimeout = 1, kErrAborted = 2, kErrFlagSpan = 3, kErrFifoEcho = 4 };
+
+// Debug FIFO integrity record of one bulk slot ("NCCL" book, s. 2.4: each
+// FIFO step carries its size and offset beside the data): the producer writes
+// the absolute step and the payload bytes of the step it put in the slot; the
+// consumer, once the tail says the step is there, checks both.
+struct alignas(16) FifoEcho {
+  uint64_t step;
+  uint32_t bytes;
+  uint32_t pad;
+};
 
 // Flag span of the line and tree FIFOs. Their flags are the low 32 bits of
 // (step + 1), so a line left from step s would match step s + 2^32, and a
@@ -81,6 +91,7 @@ struct RingArgs {
   int skip_rank;        // testing knob: workgroups of this rank return at once (-1 = none)
   int lds_stage;        // bulk: stage each step's own operand in LDS (2 x slot_bytes dynamic LDS)
   int group;            // slot steps a stage moves before the next stage runs (0 = the whole stage)
+  FifoEcho* echo;       // bulk debug: [rank][pipeline][slot] beside the FIFO, null = off
 };
 
 // Double-binary-tree all-reduce (flag-packed lines). Workgroup b of the grid
@@ -121,15 +132,14 @@ struct CopyArgs {
   int64_t block_bytes;  // bytes of one (source rank, destination rank) block
   int nranks;
   int transpose;        // 1: all-to-all; 0: rank r copies src[r] -> dst[r]
-  int vec_ok;
 };
 
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device memory p with a
 // kernel (no memset node, so that it can be captured) (copy.hip).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
-// Kernel launchers (ring_bulk.hip, ring_lines_half.hip, ring_lines_one.hip,
-// ring_lines_multi.hip, tree.hip, copy.hip).
+// Kernel launchers (ring_bulk.hip; ring_lines_inst.hip, built once per line
+// mode as _half, _one and _multi; tree.hip; copy.hip).
 hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipStream_t s);
 // Line protocols: the _half variant when no step of the launch holds more
 // than 128 lines, _one when none holds more than 256, else _multi.

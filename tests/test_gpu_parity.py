@@ -150,13 +150,18 @@ def test_all_gather(proto):
 
 
 def test_alltoall():
-    for n, cnt, dtype in ((1, 100, "float32"), (3, 1001, "bfloat16"), (8, 65_536, "bfloat16"), (4, 3, "int64")):
-        xs = _inputs(n, n * cnt, dtype, 500 + n)
-        G.say(f"alltoall N={n} count={cnt} dtype={dtype}")
+    """Blocks of every alignment: whole 16-byte vectors, 8-, 4- and 2-byte
+    units (block sizes that are no multiple of 16 bytes), and buffers that
+    start off a 16-byte boundary (shift = elements of offset)."""
+    for n, cnt, dtype, shift in ((1, 100, "float32", 0), (3, 1001, "bfloat16", 0), (8, 65_536, "bfloat16", 0),
+                                 (4, 3, "int64", 0), (5, 1001, "float32", 0), (2, 7, "int32", 0),
+                                 (4, 4096, "bfloat16", 1), (3, 2048, "float32", 3)):
+        xs = _inputs(n, n * cnt, dtype, 500 + n + shift)
+        G.say(f"alltoall N={n} count={cnt} dtype={dtype} shift={shift}")
         comm = rs.comm_init(n, 1, "auto")
         try:
-            send = [G.to_device(x, dtype) for x in xs]
-            recv = [G.empty_like_rank(n * cnt, dtype) for _ in range(n)]
+            send = [G.to_device(np.concatenate([np.zeros(shift, x.dtype), x]), dtype)[shift:] for x in xs]
+            recv = [G.empty_like_rank(n * cnt + shift, dtype)[shift:] for _ in range(n)]
             rs.alltoall(comm, send, recv)
             G.sync()
             G.check_comm_ok(comm)

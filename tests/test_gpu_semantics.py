@@ -194,6 +194,51 @@ def test_flag_span_zeroing_keeps_results(proto, algo, monkeypatch):
         rs.comm_destroy(comm)
 
 
+def test_debug_fifo_records_hold_on_every_bulk_step(monkeypatch):
+    """With RINGSIM_DEBUG_FIFO=1 every bulk slot carries (step, bytes) from
+    its producer and its consumer checks them: all-reduces (several loops,
+    ragged tails, unaligned buffers), a reduce-scatter and an all-gather stay
+    bit-exact against the oracle and no record ever disagrees."""
+    import torch
+
+    monkeypatch.setenv("RINGSIM_DEBUG_FIFO", "1")
+    comms = {c: rs.comm_init(5, c, "bulk", algo="ring", chunk_bytes=4096) for c in (1, 3)}
+    monkeypatch.delenv("RINGSIM_DEBUG_FIFO")
+    try:
+        for k, (nch, count) in enumerate([(1, 1), (3, 1000), (3, 100_003), (1, 70_001), (3, 8191)]):
+            comm = comms[nch]
+            xs = [np.random.default_rng(500 + 10 * k + r).standard_normal(count).astype(np.float32) for r in range(5)]
+            G.say(f"debug fifo: allreduce N=5 C={nch} count={count}")
+            send = [G.to_device(x, "float32") for x in xs]
+            recv = [G.empty_like_rank(count, "float32") for _ in range(5)]
+            if k == 4:  # element-aligned only: the element-wise path
+                recv = [G.empty_like_rank(count + 1, "float32")[1:] for _ in range(5)]
+            rs.allreduce(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=nch, chunk_bytes=4096)
+            for r in range(5):
+                assert G.bits_equal(G.to_host(recv[r], "float32"), want[r], "float32"), (k, r)
+        comm = comms[3]
+        rc = 30_001
+        xs = [np.random.default_rng(600 + r).integers(-1000, 1000, 5 * rc).astype(np.int32) for r in range(5)]
+        send = [G.to_device(x, "int32") for x in xs]
+        shard = [torch.empty(rc, dtype=torch.int32, device="cuda:0") for _ in range(5)]
+        full = [torch.empty(5 * rc, dtype=torch.int32, device="cuda:0") for _ in range(5)]
+        G.say("debug fifo: reduce_scatter then all_gather N=5 C=3")
+        rs.reduce_scatter(comm, send, shard)
+        rs.all_gather(comm, shard, full)
+        G.sync()
+        G.check_comm_ok(comm)
+        want = oracle.ring_reduce_scatter(xs, "sum", "int32", nchannels=3, chunk_bytes=4096)
+        for r in range(5):
+            assert np.array_equal(G.to_host(shard[r], "int32"), want[r]), r
+            assert np.array_equal(G.to_host(full[r], "int32"), np.concatenate(want)), r
+    finally:
+        for c in comms.values():
+            rs.comm_destroy(c)
+
+
 def test_comm_reuse_after_destroy_is_invalid_usage():
     import ctypes
 
