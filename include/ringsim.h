@@ -28,8 +28,8 @@
  *     be issued from one host thread and must be ordered on the device (one
  *     stream, or streams ordered by events): the FIFOs are shared state.
  *   - Calls may be captured into a HIP graph (stream capture): a call
- *     made while its stream is capturing enqueues kernel launches only (no
- *     memset, copy, event or synchronization), and every kernel reads where its FIFOs stand from
+ *     enqueues kernel launches only (no memset, copy, event or
+ *     synchronization), and every kernel reads where its FIFOs stand from
  *     the communicator's persistent step counters when it starts, so graph
  *     launches and direct calls may follow one another in any order as long
  *     as they are ordered on the device. What ringsim_comm_query reports
@@ -78,7 +78,7 @@ typedef enum {
   RINGSIM_INTERNAL_ERROR = 3,         /* a kernel timed out waiting on a peer */
   RINGSIM_INVALID_ARGUMENT = 4,       /* bad pointer, size, dtype, op, rank count */
   RINGSIM_INVALID_USAGE = 5,          /* bad / destroyed handle, impossible config */
-  RINGSIM_IN_PROGRESS = 7,            /* queried work has not finished yet */
+  RINGSIM_IN_PROGRESS = 7,            /* reserved (NCCL's nonblocking state); no call returns it */
   RINGSIM_ABORTED = 8                 /* ringsim_abort was called */
 } ringsim_result_t;
 
@@ -283,16 +283,16 @@ ringsim_result_t ringsim_all_gather(ringsim_comm_t comm, const void* const* send
 ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                   size_t count, int dtype, ringsim_stream_t stream);
 
-/* Reports the communicator's asynchronous state ("NCCL" book, ch. 2, s. 2.1:
- * the asyncResult field of ncclComm; s. 2.6: asyncResult becomes success when
- * every channel is done, and ncclCommGetAsyncError reads it): RINGSIM_SUCCESS,
- * RINGSIM_IN_PROGRESS while the latest call enqueued outside stream capture
- * has not finished and no error is known, or the error a kernel or
- * ringsim_abort left behind. Completion is tracked by an event the
- * communicator owns and records after each such call, never by the
- * caller's stream, which may have been destroyed since. Calls captured into
- * a graph record nothing: their launches are not tracked, and only the
- * errors their kernels leave are reported. */
+/* Reports the communicator's asynchronous error state ("NCCL" book, ch. 2,
+ * s. 2.1: the asyncResult field of ncclComm; s. 2.6: asyncResult turns to
+ * success when every channel is done, and ncclCommGetAsyncError reads it):
+ * RINGSIM_SUCCESS while no error is known, else the error a kernel (a wait
+ * that expired: RINGSIM_INTERNAL_ERROR) or ringsim_abort (RINGSIM_ABORTED)
+ * left behind. It says nothing about whether enqueued work has finished:
+ * that is for the caller's stream or events to tell, as PyTorch's
+ * ProcessGroupNCCL records an event after each collective on its stream
+ * ("NCCL 专家课程 29: ProcessGroupNCCL、Stream、Event 与 Work"). The library
+ * keeps no stream handle. Host only, never blocks. */
 ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error);
 
 /* Raises the abort word that every spinning kernel polls ("NCCL" book, ch. 3,

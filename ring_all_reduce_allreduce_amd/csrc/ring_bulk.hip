@@ -174,7 +174,7 @@ __device__ __forceinline__ void stage_to_lds(const char* src, int64_t nv, u32x4*
   }
 }
 
-template <int DT, int OP, int MODE>
+template <int DT, int OP, int MODE, int VAR>
 __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int64_t A = 16 / (int64_t)sizeof(T);
@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   // whatever the chunk size.
   const int64_t slice = a.slot_bytes / (int64_t)sizeof(T);
   StepIter<DT, MODE> it;
-  it.init(a, p.r, p.c, p.w, slice, a.group > 0 ? (int64_t)a.group * slice : 0);
+  it.init(a, p.r, p.c, p.w, slice, VAR == kBulkGrouped ? (int64_t)a.group * slice : 0);
   StepIter<DT, MODE> nx = it;
   if (!nx.done) nx.next();
   const bool lds = a.lds_stage && a.vec_ok;
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   // writes (null unless the communicator was created with RINGSIM_DEBUG_FIFO).
   FifoEcho* echo_in = nullptr;
   FifoEcho* echo_out = nullptr;
-  if (a.echo) {
+  if constexpr (VAR == kBulkEcho) {
     const int fpipe = p.c * a.fifo_mul + p.w;
     echo_in = a.echo + ((int64_t)p.r * a.fifo_stride + fpipe) * a.nslots;
     echo_out = a.echo + ((int64_t)p.nxt * a.fifo_stride + fpipe) * a.nslots;
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
         known_tail = wait_geq(&p.in_ctr->tail, need_tail, wc);
         stop = known_tail == 0;
       }
-      if (!stop && recv && echo_in) {
+      if (VAR == kBulkEcho && !stop && recv) {
         // Debug: the slot must hold the step and size this step expects.
         const FifoEcho* e = echo_in + in_slot;
         const uint64_t step = __hip_atomic_load(&e->step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
     char* fout = send ? p.out_fifo + (int64_t)out_slot * a.slot_bytes : nullptr;
     move_slice<DT, OP>(ns, fin, it.use_local ? it.local() : nullptr, fout, it.store ? it.out() : nullptr,
                        a.slot_bytes, a.vec_ok, lds && it.use_local ? lds_stage + buf * stage_vecs : nullptr);
-    if (send && echo_out && threadIdx.x == 0) {
+    if (VAR == kBulkEcho && send && threadIdx.x == 0) {
       // Debug: completes with the slot's data, before the tail is published.
       FifoEcho* e = echo_out + out_slot;
       __hip_atomic_store(&e->step, out_base + nsent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -298,7 +298,18 @@ struct BulkLaunch {
   static hipError_t run(const RingArgs& a, hipStream_t s) {
     const int grid = a.nranks * a.nchannels * a.wpc;
     const size_t lds = a.lds_stage ? 2 * (size_t)a.slot_bytes : 0;
-    hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE>), dim3(grid), dim3(kThreads), lds, s, a);
+    if (a.group > 0) {
+      if constexpr (MODE != kAllReduce) {
+        return hipErrorInvalidValue;  // step groups serve the all-reduce only
+      } else {
+        if (a.echo) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE, kBulkGrouped>), dim3(grid), dim3(kThreads), lds, s, a);
+      }
+    } else if (a.echo) {
+      hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE, kBulkEcho>), dim3(grid), dim3(kThreads), lds, s, a);
+    } else {
+      hipLaunchKernelGGL((ring_bulk_kernel<DT, OP, MODE, kBulkPlain>), dim3(grid), dim3(kThreads), lds, s, a);
+    }
     return hipGetLastError();
   }
 };
@@ -312,11 +323,16 @@ hipError_t launch_ring_bulk(const RingArgs& a, int mode, int dtype, int op, hipS
 int bulk_blocks_per_cu(size_t lds_bytes) {
   int m = 1 << 30;
   auto acc = [&](int v) { m = v < m ? v : m; };
-#define RS_OCC_BULK(DT)                                                            \
-  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce>, lds_bytes));        \
-  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_MAX, kAllReduce>, lds_bytes));        \
-  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_PROD, kReduceScatter>, lds_bytes));   \
-  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllGather>, lds_bytes));
+#define RS_OCC_BULK(DT)                                                                    \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce, kBulkPlain>, lds_bytes));      \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_MAX, kAllReduce, kBulkPlain>, lds_bytes));      \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_PROD, kReduceScatter, kBulkPlain>, lds_bytes)); \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllGather, kBulkPlain>, lds_bytes));      \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce, kBulkGrouped>, lds_bytes));    \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_MAX, kAllReduce, kBulkGrouped>, lds_bytes));    \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllReduce, kBulkEcho>, lds_bytes));       \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_PROD, kReduceScatter, kBulkEcho>, lds_bytes));  \
+  acc(occupancy(ring_bulk_kernel<DT, RINGSIM_SUM, kAllGather, kBulkEcho>, lds_bytes));
   RS_OCC_BULK(RINGSIM_INT32)
   RS_OCC_BULK(RINGSIM_INT64)
   RS_OCC_BULK(RINGSIM_FLOAT32)

@@ -131,11 +131,6 @@ struct ringsim_comm {
   FifoCtr* tree_ctr;
   size_t tree_ctr_bytes;
   ringsim_result_t sticky;
-  // Recorded on the call's stream after every call enqueued outside stream
-  // capture: completion is tracked without keeping the caller's stream,
-  // which may be destroyed before the communicator is queried.
-  hipEvent_t done_event;
-  bool event_recorded;
   uint64_t end_magic;
 };
 
@@ -519,16 +514,6 @@ bool is_capturing(hipStream_t s) {
   return cap != hipStreamCaptureStatusNone;
 }
 
-// After a call's kernels are enqueued: record the completion event, unless
-// the stream is being captured (a graph's launches are not tracked; an event
-// record would also become a node of the graph).
-ringsim_result_t note_enqueued(ringsim_comm* c, hipStream_t s, bool capturing, ringsim_result_t res) {
-  if (res != RINGSIM_SUCCESS || capturing) return res;
-  if (hipEventRecord(c->done_event, s) != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
-  c->event_recorded = true;
-  return RINGSIM_SUCCESS;
-}
-
 ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
                                  int dtype, int op, hipStream_t s, bool vec, bool capturing);
 
@@ -547,8 +532,7 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   if ((res = check_device(c)) != RINGSIM_SUCCESS) return res;
   hipStream_t s = static_cast<hipStream_t>(stream);
   c->calls++;
-  const bool capturing = is_capturing(s);
-  return note_enqueued(c, s, capturing, run_ring_launch(c, mode, sb, rb, count, dtype, op, s, vec, capturing));
+  return run_ring_launch(c, mode, sb, rb, count, dtype, op, s, vec, is_capturing(s));
 }
 
 ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
@@ -615,8 +599,6 @@ void free_comm_memory(ringsim_comm* c) {
   c->tree_ctr = nullptr;
   if (c->dev_abort) (void)hipFree(c->dev_abort);
   if (c->host_words) (void)hipHostFree(c->host_words);
-  if (c->done_event) (void)hipEventDestroy(c->done_event);
-  c->done_event = nullptr;
   c->fifo = c->flag_fifo = nullptr;
   c->ctr = nullptr;
   c->dev_abort = nullptr;
@@ -866,7 +848,6 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
             hipMalloc((void**)&c->dev_abort, 256) == hipSuccess &&
             hipHostMalloc((void**)&c->host_words, 256, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   if (ok) ok = hipHostGetDevicePointer((void**)&c->host_words_dev, c->host_words, 0) == hipSuccess;
-  if (ok) ok = hipEventCreateWithFlags(&c->done_event, hipEventDisableTiming) == hipSuccess;
   if (ok && c->echo_bytes) ok = hipMalloc((void**)&c->echo, c->echo_bytes) == hipSuccess;
   if (ok && tree_fifos) {
     ok = hipMalloc((void**)&c->tree_fifo, c->tree_fifo_bytes) == hipSuccess &&
@@ -994,28 +975,18 @@ ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbu
   ca.block_bytes = (int64_t)count * esize;
   ca.nranks = (int)n;
   ca.transpose = 1;
-  return note_enqueued(comm, s, is_capturing(s),
-                       launch_copy(ca, s) == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR);
+  return launch_copy(ca, s) == hipSuccess ? RINGSIM_SUCCESS : RINGSIM_UNHANDLED_DEVICE_ERROR;
 }
 
 ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* async_error) {
   ringsim_result_t res = check_comm(comm);
   if (res != RINGSIM_SUCCESS) return res;
   if (!async_error) return RINGSIM_INVALID_ARGUMENT;
-  ringsim_result_t st = poll_async(comm);
-  // Completion of the latest call enqueued outside capture, through the
-  // communicator's own event (never the caller's stream).
-  if (st == RINGSIM_SUCCESS && comm->event_recorded) {
-    const hipError_t q = hipEventQuery(comm->done_event);
-    if (q == hipErrorNotReady) {
-      st = RINGSIM_IN_PROGRESS;
-    } else if (q != hipSuccess) {
-      st = RINGSIM_UNHANDLED_DEVICE_ERROR;
-    } else {
-      st = poll_async(comm);  // the kernel may have just finished with an error
-    }
-  }
-  *async_error = st;
+  // Errors only, as ncclCommGetAsyncError reports the communicator's
+  // asyncResult: whether enqueued work has finished is for the caller's
+  // streams and events to tell (a per-call event would cost every call
+  // 2.6-4.3 us of device time on MI355X).
+  *async_error = poll_async(comm);
   return RINGSIM_SUCCESS;
 }
 

@@ -42,8 +42,10 @@ def _sleep_cycles_for(ms):
 
 def test_call_returns_before_completion_and_keeps_stream_order():
     """A 16 MiB all-reduce enqueued behind a ~50 ms device sleep returns to the
-    host at once, reports IN_PROGRESS, and is correct after the stream syncs
-    (the call behaves like ncclAllReduce under ProcessGroupNCCL)."""
+    host at once (an event recorded after it has not completed, and the
+    communicator knows no error), and is correct after the stream syncs (the
+    call behaves like ncclAllReduce under ProcessGroupNCCL, whose Work tracks
+    completion with an event on the stream)."""
     import torch
 
     n, count = 4, 4 << 20
@@ -60,12 +62,16 @@ def test_call_returns_before_completion_and_keeps_stream_order():
         t0 = time.perf_counter()
         rs.allreduce(comm, send, recv)
         t_call = time.perf_counter() - t0
+        done = torch.cuda.Event()
+        done.record()
         state = rs.get_async_error(comm)
+        running = not done.query()
         t1 = time.perf_counter()
         G.sync()
         t_sync = time.perf_counter() - t1
         assert t_call < 0.010, t_call
-        assert state == 7, state  # IN_PROGRESS
+        assert running
+        assert state == rs.SUCCESS, state
         assert t_sync > 0.020, t_sync
         assert rs.get_async_error(comm) == rs.SUCCESS
         want = oracle.ring_allreduce(xs, "sum", "float32", nchannels=4)
@@ -147,8 +153,11 @@ def test_abort_stops_a_stalled_collective(monkeypatch):
         recv = [torch.zeros(count, device="cuda:0") for _ in range(n)]
         G.say("skip rank 1, timeout 20 s, abort after 100 ms")
         rs.allreduce(comm, send, recv)
+        done = torch.cuda.Event()
+        done.record()
         time.sleep(0.1)
-        assert rs.get_async_error(comm) == 7  # still spinning
+        assert not done.query()  # still spinning
+        assert rs.get_async_error(comm) == rs.SUCCESS  # no wait has given up yet
         t0 = time.perf_counter()
         rs.abort(comm)
         G.sync()
