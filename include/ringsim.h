@@ -210,6 +210,11 @@ typedef struct {
  * init) keeps a (step, bytes) record beside every bulk FIFO slot, written by
  * its producer and checked by its consumer ("NCCL" book, s. 2.4: the size and
  * offset each FIFO step carries); a mismatch leaves RINGSIM_INTERNAL_ERROR.
+ * RINGSIM_ROCTX=1 (read at the first call) puts a roctx range named after
+ * the call around every communicator and collective call (not the
+ * allocation-free one), loading the roctx library at run time ("NCCL" book,
+ * ch. 3, s. 3.1: an NVTX mark at every API entry); rocprofv3 --marker-trace
+ * shows them beside the kernels.
  * Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
  * the workgroups of simulated rank r return at once, so that the bounded
  * waits of its neighbours expire and the failure path can be exercised. */

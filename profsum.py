@@ -50,25 +50,57 @@ def kernel_stats(path: str) -> list[dict]:
         return list(csv.DictReader(f))
 
 
+def markers_report(a) -> None:
+    """The kernel trace statistics and the roctx ranges (count, mean and
+    maximum host duration per name) of one run."""
+    rows = kernel_stats(a.stats)
+    ranges: dict[str, list[float]] = {}
+    with open(a.markers) as f:
+        for r in csv.DictReader(f):
+            ranges.setdefault(r["Function"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    argv = [x.replace(a.out_dir, "OUT") if a.out_dir else x for x in sys.argv[1:]]
+    lines = [f"# {a.title or a.name}", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += [f"    {c}" for c in a.command]
+    lines += ["", "Summarised with (OUT = the directory of the run above):", "",
+              "    python3 profsum.py " + " ".join(shlex.quote(x) for x in argv), "",
+              "## roctx ranges (host time of each library call)", "",
+              "| range | calls | mean us | max us |", "|---|---|---|---|"]
+    for name, d in sorted(ranges.items()):
+        lines.append(f"| `{name}` | {len(d)} | {statistics.mean(d):.1f} | {max(d):.1f} |")
+    lines += ["", "## Kernel trace statistics", "", "| kernel | calls | avg us | min us | max us | share |",
+              "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines.append("")
+    with open(a.report, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--name", required=True)
     ap.add_argument("--kernel", required=True, help="substring of the kernel name to summarise")
     ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-fetch", required=True)
-    ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--fetch", default="")
+    ap.add_argument("--write", default="")
+    ap.add_argument("--copy-fetch", default="")
+    ap.add_argument("--copy-write", default="")
     ap.add_argument("--dram", default="", help="counter_collection.csv of the DRAM-request counter run")
     ap.add_argument("--copy-dram", default="", help="the same run of the copy calibration")
     ap.add_argument("--out-dir", default="", help="shown as OUT in the report's copy of this command line")
-    ap.add_argument("--hash", required=True)
-    ap.add_argument("--algorithmic-bytes", type=int, required=True)
+    ap.add_argument("--hash", default="")
+    ap.add_argument("--algorithmic-bytes", type=int, default=0)
     ap.add_argument("--report", required=True)
-    ap.add_argument("--traffic", required=True)
+    ap.add_argument("--traffic", default="")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--title", default="")
+    ap.add_argument("--markers", default="", help="marker_api_trace.csv of a --marker-trace run: report the "
+                                                  "roctx ranges instead of the traffic")
     a = ap.parse_args()
+    if a.markers:
+        return markers_report(a)
 
     fetch = per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
     write = per_dispatch(a.write, a.kernel, "WRITE_SIZE")

@@ -8,6 +8,7 @@
 // the algorithm, protocol and workgroups per channel with the cost model
 // (ring_model.h), fill one kernel-argument block and enqueue one kernel on
 // the caller's stream. Nothing waits for the device.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -54,6 +55,55 @@ int log_level() {
       std::fprintf(stderr, "\n");                          \
     }                                                      \
   } while (0)
+
+// roctx ranges around the API calls ("NCCL" book, ch. 3, s. 3.1 and the
+// enqueue chapter: an NVTX mark at every API entry). With RINGSIM_ROCTX=1
+// the library loads a roctx library at its first call and pushes a range
+// named after the call for its duration; rocprofv3 --marker-trace shows them
+// next to the kernels. Off by default, at the cost of one predictable branch
+// per call; nothing is linked in.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx x;
+    const char* e = std::getenv("RINGSIM_ROCTX");
+    if (!e || !*e || !std::strcmp(e, "0")) return x;
+    for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"}) {
+      void* h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+      if (!h) continue;
+      x.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+      x.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+      if (x.push && x.pop) {
+        RS_LOG(kLogInfo, "roctx ranges on (%s)", lib);
+        return x;
+      }
+      x = Roctx{};
+    }
+    RS_LOG(kLogWarn, "RINGSIM_ROCTX is set but no roctx library could be loaded");
+    return x;
+  }();
+  return r;
+}
+
+// A range for the lifetime of the object (one API call).
+class RoctxRange {
+ public:
+  explicit RoctxRange(const char* name) : on_(roctx().push != nullptr) {
+    if (on_) roctx().push(name);
+  }
+  ~RoctxRange() {
+    if (on_) roctx().pop();
+  }
+  RoctxRange(const RoctxRange&) = delete;
+  RoctxRange& operator=(const RoctxRange&) = delete;
+
+ private:
+  const bool on_;
+};
 
 long env_long(const char* name, long dflt) {
   const char* e = std::getenv(name);
@@ -706,6 +756,7 @@ ringsim_result_t ringsim_comm_init(ringsim_comm_t* comm, int nranks, int nchanne
 
 ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int nchannels, int proto,
                                           const ringsim_config_t* user_cfg) {
+  const RoctxRange range("ringsim_comm_init");
   if (!comm) return RINGSIM_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > RINGSIM_MAX_RANKS) return RINGSIM_INVALID_ARGUMENT;
   if (nchannels < 1 || nchannels > RINGSIM_MAX_CHANNELS) return RINGSIM_INVALID_ARGUMENT;
@@ -884,6 +935,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
 }
 
 ringsim_result_t ringsim_comm_destroy(ringsim_comm_t comm) {
+  const RoctxRange range("ringsim_comm_destroy");
   ringsim_result_t res = check_comm(comm);
   if (res != RINGSIM_SUCCESS) return res;
   {
@@ -936,21 +988,25 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
 
 ringsim_result_t ringsim_allreduce(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                    size_t count, int dtype, int op, ringsim_stream_t stream) {
+  const RoctxRange range("ringsim_allreduce");
   return run_ring(comm, kAllReduce, sendbufs, recvbufs, count, dtype, op, stream);
 }
 
 ringsim_result_t ringsim_reduce_scatter(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                         size_t recvcount, int dtype, int op, ringsim_stream_t stream) {
+  const RoctxRange range("ringsim_reduce_scatter");
   return run_ring(comm, kReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream);
 }
 
 ringsim_result_t ringsim_all_gather(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                     size_t sendcount, int dtype, ringsim_stream_t stream) {
+  const RoctxRange range("ringsim_all_gather");
   return run_ring(comm, kAllGather, sendbufs, recvbufs, sendcount, dtype, RINGSIM_SUM, stream);
 }
 
 ringsim_result_t ringsim_alltoall(ringsim_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                                   size_t count, int dtype, ringsim_stream_t stream) {
+  const RoctxRange range("ringsim_alltoall");
   ringsim_result_t res = check_comm(comm);
   if (res != RINGSIM_SUCCESS) return res;
   if ((res = poll_async(comm)) != RINGSIM_SUCCESS) return res;
@@ -991,6 +1047,7 @@ ringsim_result_t ringsim_get_async_error(ringsim_comm_t comm, ringsim_result_t* 
 }
 
 ringsim_result_t ringsim_abort(ringsim_comm_t comm) {
+  const RoctxRange range("ringsim_abort");
   ringsim_result_t res = check_comm(comm);
   if (res != RINGSIM_SUCCESS) return res;
   __atomic_store_n(&comm->host_words[0], 1u, __ATOMIC_RELEASE);
