@@ -351,8 +351,8 @@ ringsim_result_t ringsim_debug_tree_model(int nranks, int tree_channels, size_t 
  * FIFOs and counters were last zeroed, and zeroes them (a kernel on the
  * call's stream) before a call that could take a counter past 2^31; a call
  * whose own bound exceeds 2^31 returns RINGSIM_INVALID_USAGE. Calls captured
- * into a graph are not counted, and a kernel that starts from a counter past
- * 2^31 (only graph replays can take it there) leaves RINGSIM_INTERNAL_ERROR
+ * into a graph are not counted, and a kernel that leaves a counter past 2^31
+ * (only graph replays can take it there) leaves RINGSIM_INTERNAL_ERROR
  * (RINGSIM_DEBUG_FLAG_SPAN=n lowers the bound that triggers the zeroing to n
  * steps, for tests). Writes to *steps the bound for one call: `algo`
  * RINGSIM_ALGO_RING with `proto` RINGSIM_PROTO_FLAG or _WIDE and `coll`

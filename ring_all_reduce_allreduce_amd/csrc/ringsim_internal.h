@@ -69,9 +69,10 @@ struct alignas(16) FifoEcho {
 // (step + 1), so a line left from step s would match step s + 2^32, and a
 // zeroed line matches step 2^32 - 1. The host zeroes a communicator's line
 // (or tree) FIFOs and counters before any of its calls could take a counter
-// past kFlagSpanGuard + the call's steps (< 2^32 - 1); a kernel that starts
-// from a counter above kFlagSpanGuard (only launches the host does not see,
-// graph replays, can get there) records kErrFlagSpan.
+// past kFlagSpanGuard; a kernel that leaves a counter above it (only
+// launches the host does not see, graph replays, can get there) records
+// kErrFlagSpan, its own results still exact (a call moves fewer than 2^31
+// steps, so its counters stay below 2^32 - 1).
 constexpr uint64_t kFlagSpanGuard = 1ull << 31;
 
 struct RingArgs {

@@ -155,7 +155,6 @@ __global__ void __launch_bounds__(kThreads) tree_line_kernel(TreeArgs a) {
     for (int j = 0; j < 2; ++j) {
       s_base[j] = j < nin ? ld_relaxed(&in_ctr[j]->head) : 0;
       s_base[2 + j] = j < nout ? ld_relaxed(&out_ctr[j]->tail) : 0;
-      if (s_base[j] > kFlagSpanGuard || s_base[2 + j] > kFlagSpanGuard) raise_error(wait_ctx(a), kErrFlagSpan);
     }
   }
   __syncthreads();
@@ -238,6 +237,10 @@ __global__ void __launch_bounds__(kThreads) tree_line_kernel(TreeArgs a) {
       if (j < nin) st_relaxed(&in_ctr[j]->head, in_base[j] + nsl);
       if (j < nout) st_relaxed(&out_ctr[j]->tail, out_base[j] + nsl);
     }
+    // Past the flag span (graph replays only), checked off the step path.
+    if ((nin > 0 && in_base[0] + nsl > kFlagSpanGuard) || (nout > 0 && out_base[0] + nsl > kFlagSpanGuard) ||
+        (nin > 1 && in_base[1] + nsl > kFlagSpanGuard) || (nout > 1 && out_base[1] + nsl > kFlagSpanGuard))
+      raise_error(wc, kErrFlagSpan);
   }
 }
 
