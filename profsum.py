@@ -50,6 +50,30 @@ def kernel_stats(path: str) -> list[dict]:
         return list(csv.DictReader(f))
 
 
+def trace_report(a) -> None:
+    """The kernel trace statistics of one run (no counters), with the
+    average of the kernel named by --kernel."""
+    rows = kernel_stats(a.stats)
+    argv = [x.replace(a.out_dir, "OUT") if a.out_dir else x for x in sys.argv[1:]]
+    lines = [f"# {a.title or a.name}", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += [f"    {c}" for c in a.command]
+    lines += ["", "Summarised with (OUT = the directory of the run above):", "",
+              "    python3 profsum.py " + " ".join(shlex.quote(x) for x in argv), "",
+              "## Kernel trace statistics", "", "| kernel | calls | avg us | min us | max us | share |",
+              "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    target = [r for r in rows if a.kernel in r["Name"]]
+    if target:
+        lines += ["", f"- `{a.kernel}`: {target[0]['Calls']} launches, average "
+                      f"{float(target[0]['AverageNs']) / 1e3:.1f} us"]
+    lines.append("")
+    with open(a.report, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def markers_report(a) -> None:
     """The kernel trace statistics and the roctx ranges (count, mean and
     maximum host duration per name) of one run."""
@@ -101,6 +125,8 @@ def main() -> None:
     a = ap.parse_args()
     if a.markers:
         return markers_report(a)
+    if not a.fetch:
+        return trace_report(a)
 
     fetch = per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
     write = per_dispatch(a.write, a.kernel, "WRITE_SIZE")
