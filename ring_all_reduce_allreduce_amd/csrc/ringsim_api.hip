@@ -215,7 +215,7 @@ ringsim_result_t poll_async(ringsim_comm* c) {
     RS_LOG(kLogWarn, "a bulk FIFO slot held another step or size than its consumer expected");
   } else if (kerr == kErrFlagSpan) {
     c->sticky = RINGSIM_INTERNAL_ERROR;
-    RS_LOG(kLogWarn, "a line or tree kernel started past the flag span (calls replayed from graphs, untracked)");
+    RS_LOG(kLogWarn, "a line or tree kernel left a counter past the flag span (calls replayed from graphs)");
   }
   return c->sticky;
 }
@@ -467,6 +467,17 @@ bool auto_picks_tree(const ringsim_comm* c, int dtype, int op, size_t count) {
   return tree_plan(c, count * (size_t)dtype_size(dtype), dtype_size(dtype)).us < pick_proto(c, kAllReduce, count, dtype).us;
 }
 
+// Is `s` being captured into a graph? (A stream the runtime cannot tell
+// about is taken as not captured.)
+bool is_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cap != hipStreamCaptureStatusNone;
+}
+
 // Flag span bookkeeping. An upper bound on the steps any one FIFO of a ring
 // line launch moves ("NCCL" book, s. 2.3: a loop of N chunks, 2(N-1) sending
 // stages for the all-reduce, N-1 for reduce-scatter and all-gather): loop l
@@ -498,17 +509,17 @@ uint64_t tree_steps_bound(int64_t count, int esize) {
 // Before a line or tree launch of `bound` steps per FIFO: zero that family's
 // FIFOs and counters first if the steps since the last zeroing could take a
 // counter past the span (then flags restart at 1 over all-zero lines). Not
-// while the stream is captured: a zeroing kernel in a graph would run at
-// every replay; replayed launches are not counted here, and a kernel that
-// starts past kFlagSpanGuard reports it.
-ringsim_result_t guard_span(ringsim_comm* c, bool tree, uint64_t bound, bool capturing, hipStream_t s) {
+// while the stream is captured (a zeroing kernel in a graph would run at
+// every replay): the zeroing then waits for the next call made outside
+// capture. A captured call counts once, its replays not at all; a kernel
+// that leaves a counter past kFlagSpanGuard reports it.
+ringsim_result_t guard_span(ringsim_comm* c, bool tree, uint64_t bound, hipStream_t s) {
   if (bound > kFlagSpanGuard) {
     RS_LOG(kLogWarn, "a line or tree call of %llu steps per FIFO exceeds the flag span", (unsigned long long)bound);
     return RINGSIM_INVALID_USAGE;
   }
-  if (capturing) return RINGSIM_SUCCESS;
   uint64_t& span = tree ? c->tree_span : c->line_span;
-  if (span + bound > c->span_limit) {
+  if (span + bound > c->span_limit && !is_capturing(s)) {
     hipError_t e = tree ? launch_zero(c->tree_fifo, c->tree_fifo_bytes, s) : launch_zero(c->flag_fifo, c->flag_fifo_bytes, s);
     if (e == hipSuccess) e = tree ? launch_zero(c->tree_ctr, c->tree_ctr_bytes, s) : launch_zero(c->ctr, c->ctr_bytes, s);
     if (e != hipSuccess) return RINGSIM_UNHANDLED_DEVICE_ERROR;
@@ -553,19 +564,6 @@ ringsim_result_t launch_tree(ringsim_comm* c, const void* const* sb, void* const
   return RINGSIM_SUCCESS;
 }
 
-// Is `s` being captured into a graph? (A stream the runtime cannot tell
-// about is taken as not captured.)
-bool is_capturing(hipStream_t s) {
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
-    (void)hipGetLastError();
-    return false;
-  }
-  return cap != hipStreamCaptureStatusNone;
-}
-
-ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
-                                 int dtype, int op, hipStream_t s, bool vec, bool capturing);
 
 ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
                           int dtype, int op, ringsim_stream_t stream) {
@@ -582,13 +580,6 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   if ((res = check_device(c)) != RINGSIM_SUCCESS) return res;
   hipStream_t s = static_cast<hipStream_t>(stream);
   c->calls++;
-  return run_ring_launch(c, mode, sb, rb, count, dtype, op, s, vec, is_capturing(s));
-}
-
-ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* sb, void* const* rb, size_t count,
-                                 int dtype, int op, hipStream_t s, bool vec, bool capturing) {
-  const int esize = dtype_size(dtype);
-  const int64_t n = c->nranks;
   if (n == 1) {
     // A single rank is a local copy ("NCCL" book, enqueue chapter, taskAppend).
     return launch_local_copy(c, sb, rb, count * esize, s);
@@ -599,7 +590,7 @@ ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* s
     c->last_algo = tree ? RINGSIM_ALGO_TREE : RINGSIM_ALGO_RING;
     c->last_tree_channels = 0;
     if (tree) {
-      const ringsim_result_t g = guard_span(c, true, tree_steps_bound((int64_t)count, esize), capturing, s);
+      const ringsim_result_t g = guard_span(c, true, tree_steps_bound((int64_t)count, esize), s);
       return g != RINGSIM_SUCCESS ? g : launch_tree(c, sb, rb, count, dtype, op, vec, s);
     }
   }
@@ -621,7 +612,7 @@ ringsim_result_t run_ring_launch(ringsim_comm* c, int mode, const void* const* s
     const int lp = proto == RINGSIM_PROTO_WIDE ? kLineWide : kLineFlag;
     const int64_t payload = lp == kLineWide && dtype != RINGSIM_INT64 ? 12 : 8;
     const ringsim_result_t g = guard_span(
-        c, false, line_steps_bound(mode, a.count, a.nranks, a.nchannels, a.chunk, esize, payload), capturing, s);
+        c, false, line_steps_bound(mode, a.count, a.nranks, a.nchannels, a.chunk, esize, payload), s);
     if (g != RINGSIM_SUCCESS) return g;
     c->last_wpc = a.wpc;
     e = pc.plan.mode == kHostLinesHalf  ? launch_ring_lines_half(a, lp, mode, dtype, op, s)
