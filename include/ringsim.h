@@ -160,7 +160,11 @@ typedef enum {
 /* Tunables; zero fields take the default. */
 typedef struct {
   size_t chunk_bytes;          /* ring chunk per channel; default 524288; multiple of 16 */
-  int workgroups_per_channel;  /* workgroups per (rank, channel); default chosen from the CU count */
+  int workgroups_per_channel;  /* BULK: workgroups per (rank, channel); default 0 = the most the CU count
+                                  suggests (two per CU), of which a call with short stages takes fewer
+                                  (about one per 4 KiB of a channel's stage, at least two, channels x
+                                  workgroups a multiple of 8); a configured count is used by every
+                                  call; env RINGSIM_WPC */
   size_t slot_bytes;           /* bulk FIFO slot; default 32768; multiple of 4096 */
   int nslots;                  /* bulk FIFO depth; default 8 (NCCL_STEPS) */
   int timeout_ms;              /* bound on any single wait; default 10000, env RINGSIM_TIMEOUT_MS */
@@ -177,7 +181,7 @@ typedef struct {
   int nranks;
   int nchannels;
   int proto;
-  int workgroups_per_channel;
+  int workgroups_per_channel;  /* BULK: the most a call takes */
   int nslots;
   int device;
   size_t chunk_bytes;

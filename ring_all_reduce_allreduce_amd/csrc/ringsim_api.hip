@@ -134,6 +134,7 @@ struct ringsim_comm {
   int pipe_mul;     // counter pipelines per channel: max(wpc, line_wpc_max)
   int line_wpc_max; // most workgroups per channel a line launch may take (power of two)
   int line_wpc_cfg; // configured line workgroups per channel, 0 = per call
+  int wpc_cfg;      // bulk workgroups per channel were configured: no per-call choice
   int line_per_cu[3];  // resident line workgroups per CU: multi, one, half kernels
   int nslots;
   int device;
@@ -267,25 +268,27 @@ int model_proto(int proto) {
   return proto == RINGSIM_PROTO_FLAG ? kModelFlag : proto == RINGSIM_PROTO_WIDE ? kModelWide : kModelBulk;
 }
 
-// Fills the protocol-dependent launch geometry; line_wpc is the workgroup
-// count of a line launch (1, 2, 4 or 8). The flag FIFO holds one array per
-// count, in increasing order, each [rank][channel][part][slot] with
-// kFlagSlots slots of kFlagSlotBytes per part.
-void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int line_wpc = 1) {
+// Fills the protocol-dependent launch geometry; wpc is the workgroup count
+// of the launch: for a line launch 1, 2, 4 or 8 (the flag FIFO holds one
+// array per count, in increasing order, each [rank][channel][part][slot] with
+// kFlagSlots slots of kFlagSlotBytes per part); for a bulk launch at most the
+// communicator's count, whose pipelines (counters and FIFOs) keep their
+// places: a launch with fewer leaves the others' counters as they are.
+void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int wpc) {
   a->chunk = (int64_t)c->chunk_bytes / esize;
   if (proto == RINGSIM_PROTO_FLAG || proto == RINGSIM_PROTO_WIDE) {
     const size_t nc = (size_t)c->nranks * c->nchannels;
     size_t off = 0;
-    for (int w = 1; w < line_wpc; w *= 2) off += nc * (size_t)line_level_bytes(w);
-    a->wpc = line_wpc;
+    for (int w = 1; w < wpc; w *= 2) off += nc * (size_t)line_level_bytes(w);
+    a->wpc = wpc;
     a->fifo = c->flag_fifo + off;
-    a->fifo_stride = c->nchannels * line_wpc;
-    a->fifo_mul = line_wpc;
+    a->fifo_stride = c->nchannels * wpc;
+    a->fifo_mul = wpc;
     a->nslots = kFlagSlots;
     a->slot_bytes = kFlagSlotBytes;
     a->group = kLineGroupSteps;
   } else {
-    a->wpc = c->wpc;
+    a->wpc = wpc;
     a->ctr = c->bulk_ctr;
     a->pipe_stride = c->nchannels * c->wpc;
     a->pipe_mul = c->wpc;
@@ -348,6 +351,30 @@ RingArgs call_shape(const ringsim_comm* c, size_t count, int esize) {
   return a;
 }
 
+// Bulk workgroups per channel of one call. A configured count is used as it
+// is. Otherwise a call whose stages are short takes fewer pipelines than the
+// communicator holds: about one per kBulkPartBytes of a channel's stage, at
+// least two, and rounded up so that channels x workgroups is a multiple of
+// the 8 XCDs (the rank-major workgroup ids then put every workgroup of a
+// pipeline on one XCD). A call ends with its slowest pipeline, and fewer,
+// fuller pipelines finish sooner: 8 ranks x 8 channels at 4 KiB - 512 KiB per
+// rank 31.5-32.7 us with 2 against 37-39 us with 8; 4 ranks x 4 KiB on one
+// channel 15.7 us with 8 against 17.1 us with 16. A smaller count is taken
+// only when one workgroup's stage still fits half of its FIFO.
+constexpr int64_t kBulkPartBytes = 4096;
+constexpr int kXcds = 8;
+int bulk_call_wpc(const ringsim_comm* c, const RingArgs& shape, int mode, int esize) {
+  if (c->wpc_cfg) return c->wpc;
+  RingArgs t = shape;
+  t.wpc = 1;
+  int64_t w = std::max<int64_t>(2, div_up(max_unit_bytes(t, mode, esize), kBulkPartBytes));
+  while (w < c->wpc && (c->nchannels * w) % kXcds != 0) ++w;
+  if (w >= c->wpc) return c->wpc;
+  t.wpc = (int)w;
+  if (2 * div_up(max_unit_bytes(t, mode, esize), (int64_t)c->slot_bytes) > (int64_t)c->nslots) return c->wpc;
+  return (int)w;
+}
+
 struct ProtoChoice {
   int proto;
   LinePlan plan;  // line protocols: workgroups per channel and kernel
@@ -397,7 +424,7 @@ ProtoChoice pick_proto(const ringsim_comm* c, int mode, size_t count, int dtype)
   auto bulk = [&]() {
     ProtoChoice pc;
     pc.proto = RINGSIM_PROTO_BULK;
-    pc.plan = LinePlan{c->wpc, kHostLinesMulti};
+    pc.plan = LinePlan{bulk_call_wpc(c, a, mode, esize), kHostLinesMulti};
     pc.us = bulk_model_us(RingModel(), mode, c->nranks, bytes);
     return pc;
   };
@@ -841,6 +868,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->wpc = wpc;
   c->line_wpc_max = line_wpc_max;
   c->line_wpc_cfg = cfg.line_workgroups_per_channel;
+  c->wpc_cfg = cfg.workgroups_per_channel != 0;
   c->pipe_mul = std::max(wpc, line_wpc_max);
   for (int k = 0; k < 3; ++k) c->line_per_cu[k] = line_per_cu[k];
   c->nslots = nslots;

@@ -446,3 +446,50 @@ def test_line_workgroup_counts_switch_on_one_comm(proto):
             _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"switch count={count} wpc={lw}")
     finally:
         rs.comm_destroy(comm)
+
+
+def test_bulk_workgroup_counts_switch_on_one_comm():
+    """Bulk calls of one communicator take as many workgroups per channel as
+    their stages need (about one per 4 KiB of a channel's stage, at least
+    two, all of them for long stages): small, large and middle calls, a
+    reduce-scatter and an all-gather, in turn on one communicator, so that a
+    launch with more pipelines finds the counters that launches with fewer
+    left untouched. Fresh data every call, every result checked."""
+    n, nch, dtype = 8, 8, "float32"
+    comm = rs.comm_init(n, nch, "bulk")
+    try:
+        top = rs.comm_query(comm)["workgroups_per_channel"]
+        cases = []
+        for k, (coll, count) in enumerate([("allreduce", 1024), ("allreduce", (4 << 20) // 4 - 5),
+                                          ("allreduce", (1 << 20) // 4 + 3), ("allreduce", 16383),
+                                          ("reduce_scatter", 2048), ("all_gather", 3001),
+                                          ("allreduce", 1024), ("allreduce", (4 << 20) // 4 - 5)]):
+            m = count * n if coll == "reduce_scatter" else count
+            xs = _inputs(n, m, dtype, 2100 + k)
+            send = [G.to_device(x, dtype) for x in xs]
+            out = {"allreduce": m, "reduce_scatter": count, "all_gather": count * n}[coll]
+            recv = [G.empty_like_rank(out, dtype) for _ in range(n)]
+            G.say(f"bulk switch call {k}: {coll} count={count}")
+            if coll == "allreduce":
+                rs.allreduce(comm, send, recv)
+            elif coll == "reduce_scatter":
+                rs.reduce_scatter(comm, send, recv)
+            else:
+                rs.all_gather(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            cases.append((coll, xs, recv, count, rs.comm_query(comm)["last_workgroups_per_channel"]))
+        ws = [c[4] for c in cases]
+        assert ws[0] == ws[3] == ws[4] == ws[5] == ws[6] == min(2, top), ws
+        assert ws[1] == ws[7] == top, ws
+        assert min(2, top) <= ws[2] <= top, ws
+        for coll, xs, recv, count, w in cases:
+            if coll == "allreduce":
+                want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=nch)
+            elif coll == "reduce_scatter":
+                want = oracle.ring_reduce_scatter(xs, "sum", dtype, nchannels=nch)
+            else:
+                want = oracle.ring_all_gather(xs, dtype, nchannels=nch)
+            _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"bulk switch {coll} count={count} wpc={w}")
+    finally:
+        rs.comm_destroy(comm)
