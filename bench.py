@@ -657,7 +657,9 @@ def main() -> int:
             "chunk_bytes": w["chunk_bytes"],
             "buckets": nbuckets,
             "buffer_sets": w.get("buffer_sets", 1),
-            "workgroups_per_channel": info["workgroups_per_channel"],
+            # the count the timed calls took (a bulk call with short stages
+            # takes fewer than the communicator holds)
+            "workgroups_per_channel": rs.comm_query(comm)["last_workgroups_per_channel"],
             "proto": {1: "bulk", 2: "flag", 3: "wide"}.get(rs.comm_query(comm)["last_proto"], "?"),
             "parallelism": "1 GPU, simulated ranks",
         },
