@@ -160,11 +160,11 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           v[u] = u32x4{0u, 0u, 0u, 0u};
-          if (threadIdx.x + u * kThreads < nlines) v[u] = fin.load(threadIdx.x + u * kThreads);
+          if ((int)threadIdx.x + u * kThreads < nlines) v[u] = fin.load(threadIdx.x + u * kThreads);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (threadIdx.x + u * kThreads < nlines && !Slot<LP>::ready(v[u], flag_in)) pending |= 1u << u;
+          if ((int)threadIdx.x + u * kThreads < nlines && !Slot<LP>::ready(v[u], flag_in)) pending |= 1u << u;
         if (pending && !stop) {
           const uint64_t t0 = wall_clock64();
           uint32_t spins = 0, verdict = 0;

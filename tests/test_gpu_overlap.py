@@ -10,7 +10,6 @@ neighbours, so a launch whose workgroups cannot all find a compute unit
 waits for the products to free some: the test checks that both sides finish,
 that the communicator reports no error and that a bucket is bit-exact
 against the oracle, and prints each side's time alone and overlapped."""
-import numpy as np
 import pytest
 
 import oracle

@@ -2,7 +2,6 @@
 keep stream order; failures are forced from the host (a rank whose
 workgroups never take part, a short wait bound, or an abort request) and
 every kernel still drains on its own."""
-import os
 import time
 
 import numpy as np
