@@ -218,7 +218,10 @@ typedef struct {
  * the call around every communicator and collective call (not the
  * allocation-free one), loading the roctx library at run time ("NCCL" book,
  * ch. 3, s. 3.1: an NVTX mark at every API entry); rocprofv3 --marker-trace
- * shows them beside the kernels.
+ * shows them beside the kernels. RINGSIM_LDS_STAGE=0 (read at comm init)
+ * makes bulk steps load the rank's own operand beside the FIFO operand in
+ * every call; by default calls above 512 KiB per rank stage it in LDS one
+ * step ahead.
  * Testing only: RINGSIM_DEBUG_SKIP_RANK=r (read at comm init) makes
  * the workgroups of simulated rank r return at once, so that the bounded
  * waits of its neighbours expire and the failure path can be exercised. */

@@ -363,6 +363,14 @@ RingArgs call_shape(const ringsim_comm* c, size_t count, int esize) {
 // only when one workgroup's stage still fits half of its FIFO.
 constexpr int64_t kBulkPartBytes = 4096;
 constexpr int kXcds = 8;
+
+// Calls up to this many bytes per rank load the own operand of a bulk step
+// beside the FIFO operand instead of staging it in LDS one step ahead: the
+// staging's wait costs every hop more than the own operand's load latency
+// does while the memory is lightly loaded (0.5-3 us per call faster at 4,
+// 8 and 16 ranks from 4 KiB to 512 KiB per rank; from 1-2 MiB up staging
+// wins, by 6-22 us at 4-8 MiB).
+constexpr int64_t kBulkStageMinBytes = 512 * 1024;
 int bulk_call_wpc(const ringsim_comm* c, const RingArgs& shape, int mode, int esize) {
   if (c->wpc_cfg) return c->wpc;
   RingArgs t = shape;
@@ -633,6 +641,8 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   c->last_proto = proto;
   hipError_t e;
   if (proto == RINGSIM_PROTO_BULK) {
+    const int64_t rank_bytes = (int64_t)(mode == kAllReduce ? count : count * (size_t)n) * esize;
+    if (rank_bytes <= kBulkStageMinBytes) a.lds_stage = 0;
     c->last_wpc = a.wpc;
     e = launch_ring_bulk(a, mode, dtype, op, s);
   } else {
