@@ -1289,7 +1289,7 @@ ringsim_result_t ringsim_allreduce_noalloc(int nranks, int nchannels, const void
   a.fifo = d->base + kNaCtrBytes + kNaWordBytes;
   a.timeout_ticks = (uint64_t)cfg.timeout_ms * (uint64_t)d->clock_khz;
   a.skip_rank = -1;
-  a.lds_stage = 1;
+  a.lds_stage = (int64_t)count * esize > kBulkStageMinBytes;  // as ringsim_allreduce's bulk calls
   a.group = kNaGroupSteps;
   const int nclear = (int)((kNaCtrBytes + kNaWordBytes) / 16);
   hipLaunchKernelGGL(noalloc_clear, dim3((nclear + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
