@@ -183,9 +183,12 @@ __global__ void __launch_bounds__(kThreads) ring_bulk_kernel(RingArgs a) {
   if (p.r == a.skip_rank) return;  // testing knob: a rank that never shows up
   __shared__ uint64_t s_base[2];
   if (threadIdx.x == 0) {
-    // Each side's own counter tells where the previous call left this FIFO.
-    s_base[0] = ld_relaxed(&p.in_ctr->head);
-    s_base[1] = ld_relaxed(&p.out_ctr->tail);
+    // Each side's own counter tells where the previous call left this FIFO
+    // (both loads in flight before either value is used).
+    const uint64_t head = ld_relaxed(&p.in_ctr->head);
+    const uint64_t tail = ld_relaxed(&p.out_ctr->tail);
+    s_base[0] = head;
+    s_base[1] = tail;
   }
   __syncthreads();
   const uint64_t in_base = uniform64(s_base[0]);

@@ -57,8 +57,11 @@ __global__ void __launch_bounds__(kThreads) ring_line_kernel(RingArgs a) {
   __shared__ uint64_t s_base[2];
   __shared__ int s_credit;
   if (threadIdx.x == 0) {
-    s_base[0] = ld_relaxed(&p.in_ctr->head);
-    s_base[1] = ld_relaxed(&p.out_ctr->tail);
+    // Both loads in flight before either value is used.
+    const uint64_t head = ld_relaxed(&p.in_ctr->head);
+    const uint64_t tail = ld_relaxed(&p.out_ctr->tail);
+    s_base[0] = head;
+    s_base[1] = tail;
   }
   __syncthreads();
   const uint64_t in_base = uniform64(s_base[0]);

@@ -151,11 +151,15 @@ __global__ void __launch_bounds__(kThreads) tree_line_kernel(TreeArgs a) {
   __shared__ uint64_t s_base[4];
   __shared__ uint64_t s_head[2];
   if (threadIdx.x == 0) {
+    // All four loads in flight before any value is used.
+    uint64_t b[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      s_base[j] = j < nin ? ld_relaxed(&in_ctr[j]->head) : 0;
-      s_base[2 + j] = j < nout ? ld_relaxed(&out_ctr[j]->tail) : 0;
+      b[j] = j < nin ? ld_relaxed(&in_ctr[j]->head) : 0;
+      b[2 + j] = j < nout ? ld_relaxed(&out_ctr[j]->tail) : 0;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_base[j] = b[j];
   }
   __syncthreads();
   const uint64_t in_base[2] = {uniform64(s_base[0]), uniform64(s_base[1])};
