@@ -243,7 +243,7 @@ def mixed_copy_gbs(stream_bytes: int, resident_bytes: int, trials: int = 7) -> f
 
 def d2d_copy_gbs(nbytes: int = 1 << 30, reps: int = 10, trials: int = 5) -> float:
     """Device-to-device copy (read + write bytes / time, median of `trials`
-    batches of `reps` copies) as the achievable-bandwidth context of this box:
+    batches of `reps` copies) as the achievable-bandwidth context of this GPU:
     1 GiB streams from HBM; 64 MiB (source and destination both fit in the
     256 MB Infinity Cache) is the ceiling for traffic that the cache serves,
     as the FIFO slots are."""
@@ -453,8 +453,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build simulates all ranks on ONE GPU; run it with --gpus 1 "
-              "(multi-GPU rings over xGMI are not part of it)", file=sys.stderr)
+        print("bench.py: ringsim simulates all ranks on ONE GPU; run it with --gpus 1 "
+              "(rings across GPUs over xGMI are not implemented)", file=sys.stderr)
         return 2
 
     import numpy as np
