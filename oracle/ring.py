@@ -28,8 +28,7 @@ Sources (page title, section):
             broadcast and all-to-all; "In-Network SHARP Aggregation": a ring
             reduce-scatter delivers B(n-1)/n bytes to each rank.
 
-Readings taken where the pages are silent or disagree (each is listed in
-DESIGN.md as well):
+Readings taken where the pages are silent or disagree:
   R1  chunk k is seeded by rank k+1 and finished by rank k. This follows the
       chunk-id formula of [NB 2.3]; the walkthrough's prose disagrees with it
       and with itself.

@@ -25,7 +25,7 @@ rank 0 it is the smallest power of two >= N.
     (none when bit == 1). The second child is r + b for the largest b among
     bit/2, bit/4, ..., 1 with r + b < N (none when bit == 1 or no b fits).
 
-Readings taken where the pages are silent (listed in the design doc as well):
+Readings taken where the pages are silent:
   T1  Fold order at a node: its own data first, then the partial result of
       its first child, then that of its second child, rounding to the buffer
       type after every operation (reading R5 of ``oracle/ring.py``). The
