@@ -169,6 +169,18 @@ def oracle_call(w: dict, xs):
     return oracle.alltoall(xs, w["dtype"])
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 10.0):
     """The oracle, as it stands, timed on this host on the same workload:
     whole calls, repeated until about `budget_s` seconds of CPU work (at
@@ -196,7 +208,7 @@ def cpu_baseline(w: dict, xs, per_rank_bytes: int, budget_s: float = 10.0):
         "kind": "oracle",
         "sample": f"the full workload ({w['desc']}), NumPy ring replay on one thread, median of {len(times)} "
                   f"whole calls ({sum(times):.1f} s, CPU time / wall time {busy:.2f}), {t * 1e3:.3f} ms per call; host has "
-                  f"{len(os.sched_getaffinity(0))} cores available",
+                  f"{len(os.sched_getaffinity(0))} cores available ({cpu_model()})",
     }, result
 
 
