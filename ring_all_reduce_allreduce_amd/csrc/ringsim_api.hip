@@ -303,14 +303,10 @@ void fill_proto(const ringsim_comm* c, RingArgs* a, int proto, int esize, int wp
   }
 }
 
-// Longest unit (bytes) any workgroup of a ring launch moves in one stage; no
-// step is longer. The first loop of channel 0 (the longest channel) holds
-// the longest units.
+// Longest unit (bytes) any workgroup of a ring launch moves in one stage
+// (ring_model.h).
 int64_t max_unit_bytes(const RingArgs& a, int mode, int esize) {
-  const int64_t A = 16 / esize;
-  const int64_t l0 = channel_span(a.count, a.nchannels, A);
-  const int64_t cur = mode == kAllReduce ? ar_loop_chunk(l0, a.nranks, a.chunk, A) : min64(a.chunk, l0);
-  return align_up(div_up(cur, a.wpc), A) * esize;
+  return ring_max_unit_bytes(a.count, a.nranks, a.nchannels, a.chunk, mode == kAllReduce, esize, a.wpc);
 }
 
 // Line kernels by lines per step (host mirror of the device LineMode).
@@ -351,19 +347,6 @@ RingArgs call_shape(const ringsim_comm* c, size_t count, int esize) {
   return a;
 }
 
-// Bulk workgroups per channel of one call. A configured count is used as it
-// is. Otherwise a call whose stages are short takes fewer pipelines than the
-// communicator holds: about one per kBulkPartBytes of a channel's stage, at
-// least two, and rounded up so that channels x workgroups is a multiple of
-// the 8 XCDs (the rank-major workgroup ids then put every workgroup of a
-// pipeline on one XCD). A call ends with its slowest pipeline, and fewer,
-// fuller pipelines finish sooner: 8 ranks x 8 channels at 4 KiB - 512 KiB per
-// rank 31.5-32.7 us with 2 against 37-39 us with 8; 4 ranks x 4 KiB on one
-// channel 15.7 us with 8 against 17.1 us with 16. A smaller count is taken
-// only when one workgroup's stage still fits half of its FIFO.
-constexpr int64_t kBulkPartBytes = 4096;
-constexpr int kXcds = 8;
-
 // Calls up to this many bytes per rank load the own operand of a bulk step
 // beside the FIFO operand instead of staging it in LDS one step ahead: the
 // staging's wait costs every hop more than the own operand's load latency
@@ -371,16 +354,14 @@ constexpr int kXcds = 8;
 // 8 and 16 ranks from 4 KiB to 512 KiB per rank; from 1-2 MiB up staging
 // wins, by 6-22 us at 4-8 MiB).
 constexpr int64_t kBulkStageMinBytes = 512 * 1024;
-int bulk_call_wpc(const ringsim_comm* c, const RingArgs& shape, int mode, int esize) {
+
+// Bulk workgroups per channel of one call: a configured count as it is, else
+// fewer than the communicator holds when the stages are short
+// (bulk_call_wpc, ring_model.h).
+int comm_bulk_wpc(const ringsim_comm* c, const RingArgs& shape, int mode, int esize) {
   if (c->wpc_cfg) return c->wpc;
-  RingArgs t = shape;
-  t.wpc = 1;
-  int64_t w = std::max<int64_t>(2, div_up(max_unit_bytes(t, mode, esize), kBulkPartBytes));
-  while (w < c->wpc && (c->nchannels * w) % kXcds != 0) ++w;
-  if (w >= c->wpc) return c->wpc;
-  t.wpc = (int)w;
-  if (2 * div_up(max_unit_bytes(t, mode, esize), (int64_t)c->slot_bytes) > (int64_t)c->nslots) return c->wpc;
-  return (int)w;
+  return bulk_call_wpc(shape.count, shape.nranks, shape.nchannels, shape.chunk, mode == kAllReduce, esize, c->wpc,
+                       (int64_t)c->slot_bytes, c->nslots);
 }
 
 struct ProtoChoice {
@@ -432,7 +413,7 @@ ProtoChoice pick_proto(const ringsim_comm* c, int mode, size_t count, int dtype)
   auto bulk = [&]() {
     ProtoChoice pc;
     pc.proto = RINGSIM_PROTO_BULK;
-    pc.plan = LinePlan{bulk_call_wpc(c, a, mode, esize), kHostLinesMulti};
+    pc.plan = LinePlan{comm_bulk_wpc(c, a, mode, esize), kHostLinesMulti};
     pc.us = bulk_model_us(RingModel(), mode, c->nranks, bytes);
     return pc;
   };

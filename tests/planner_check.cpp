@@ -83,6 +83,17 @@ static void model(int n, int nch, double bytes) {
   std::printf("end\n");
 }
 
+// Workgroups per channel of a bulk call, and the longest unit of one
+// workgroup's stage at that count and at one workgroup.
+static void bulkw(int coll, int64_t count, int n, int nch, int64_t chunk_bytes, int esize, int wpc_max,
+                  int64_t slot_bytes, int nslots) {
+  const int64_t chunk = chunk_bytes / esize;
+  const int w = bulk_call_wpc(count, n, nch, chunk, coll == 0, esize, wpc_max, slot_bytes, nslots);
+  const int64_t unit = ring_max_unit_bytes(count, n, nch, chunk, coll == 0, esize, w);
+  const int64_t unit1 = ring_max_unit_bytes(count, n, nch, chunk, coll == 0, esize, 1);
+  std::printf("%d %lld %lld\nend\n", w, (long long)unit, (long long)unit1);
+}
+
 int main() {
   std::string cmd;
   while (std::cin >> cmd) {
@@ -95,6 +106,11 @@ int main() {
       int n;
       std::cin >> n;
       tree(n);
+    } else if (cmd == "bulkw") {
+      int coll, n, nch, esize, wpc_max, nslots;
+      long long count, chunk_bytes, slot_bytes;
+      std::cin >> coll >> count >> n >> nch >> chunk_bytes >> esize >> wpc_max >> slot_bytes >> nslots;
+      bulkw(coll, count, n, nch, chunk_bytes, esize, wpc_max, slot_bytes, nslots);
     } else if (cmd == "model") {
       int n, nch;
       double bytes;

@@ -2,7 +2,8 @@
 built into a host driver with AddressSanitizer and UndefinedBehaviorSanitizer
 (g++, CPU only): over many shapes the partition equals the oracle's own, the
 double-tree links equal the oracle's, the cost model stays finite and
-positive, and the sanitizers report nothing."""
+positive, a bulk call's workgroup count keeps its rules, and the sanitizers
+report nothing."""
 import itertools
 import os
 import shutil
@@ -87,3 +88,58 @@ def test_cost_model_under_sanitizers_is_finite(driver):
         for line in lines:
             v = float(line.split()[-1])
             assert v > 0 and v < 1e9, (shape, line)
+
+
+def _longest_unit_bytes(coll, count, n, ch, chunk_bytes, esize):
+    """Longest chunk of channel 0's first loop, from the oracle's partition."""
+    a = 16 // esize
+    lo, hi = oracle.channel_ranges(count, ch, a)[0]
+    if hi <= lo:
+        return 0
+    if coll == 0:
+        ks = oracle.allreduce_loop_chunks(hi - lo, n, chunk_bytes // esize, a)[0]
+        return max(e - b for b, e in ks) * esize
+    b, e = oracle.block_loop_ranges(hi - lo, chunk_bytes // esize)[0]
+    return (e - b) * esize
+
+
+def test_bulk_workgroups_per_call_keep_their_rules(driver):
+    """A bulk call takes the communicator's workgroup count, or fewer when its
+    stages are short: at least two, about one per 4 KiB of a channel's stage,
+    channels x workgroups a multiple of 8, and one workgroup's stage within
+    half of its FIFO; long stages take the full count. The stage length it
+    starts from is the longest chunk of the oracle's partition, rounded up to
+    whole 16-byte vectors (a bound: the library sizes channel 0 before
+    clamping it to a tiny count)."""
+    cases = []
+    for coll, count, n, ch, esize in itertools.product((0, 1), (1, 1000, 4096, 65_536, 262_144, 1 << 20, 1 << 22),
+                                                       (2, 4, 8, 16, 64), (1, 3, 8, 16), (2, 4, 8)):
+        if n * ch > 512:
+            continue
+        wpc_max = max(1, min(16, 2 * 256 // (n * ch)))
+        for slot in (4096, 32768):
+            # the communicator's FIFO depth: 8 slots, more when one
+            # workgroup's stage at the full count needs them
+            stage = -(-(-(-524_288 // wpc_max)) // 16) * 16
+            nslots = max(8, 2 * -(-stage // slot))
+            cases.append((coll, count, n, ch, 524_288, esize, wpc_max, slot, nslots))
+    blocks = _run(driver, [f"bulkw {' '.join(map(str, c))}" for c in cases])
+    assert len(blocks) == len(cases)
+    for c, lines in zip(cases, blocks):
+        coll, count, n, ch, cb, esize, wpc_max, slot, nslots = c
+        w, unit, unit1 = map(int, lines[0].split())
+        longest = _longest_unit_bytes(coll, count, n, ch, cb, esize)
+        assert longest <= unit1 < longest + 16, c
+        assert 1 <= w <= wpc_max, c
+        need = -(-unit1 // 4096)
+        if w < wpc_max:
+            assert w >= 2 and (ch * w) % 8 == 0, c
+            assert w >= need, c
+            assert 2 * -(-unit // slot) <= nslots, c
+        if need >= wpc_max:
+            assert w == wpc_max, c
+    anchors = {(0, 1024, 4, 1, 4): 8, (0, 1024, 8, 8, 4): 2, (0, 1 << 20, 8, 8, 4): 8, (0, 1024, 16, 16, 4): 2}
+    for (coll, count, n, ch, esize), want in anchors.items():
+        wpc_max = max(1, min(16, 2 * 256 // (n * ch)))
+        lines = _run(driver, [f"bulkw {coll} {count} {n} {ch} 524288 {esize} {wpc_max} 32768 8"])[0]
+        assert int(lines[0].split()[0]) == want, (coll, count, n, ch, esize)
