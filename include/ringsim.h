@@ -203,6 +203,8 @@ typedef struct {
   int last_tree_channels;              /* channels per tree of the latest all-reduce, 0 if it ran the ring */
   uint64_t line_fifo_resets;           /* times the FLAG/WIDE FIFOs and counters were zeroed (flag span) */
   uint64_t tree_fifo_resets;           /* the same for the tree FIFOs */
+  int last_group_steps;                /* BULK all-reduce: slot steps a stage of the latest ring call moved
+                                          before the next stage ran (0 = whole stages) */
 } ringsim_comm_info_t;
 
 /* Fills *cfg with the defaults ("NCCL" book, ch. 3, s. 3.5: every tunable is

@@ -106,6 +106,7 @@ class CommInfo(ctypes.Structure):
         ("last_tree_channels", ctypes.c_int),
         ("line_fifo_resets", ctypes.c_uint64),
         ("tree_fifo_resets", ctypes.c_uint64),
+        ("last_group_steps", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:

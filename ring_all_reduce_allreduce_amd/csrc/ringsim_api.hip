@@ -137,6 +137,7 @@ struct ringsim_comm {
   int wpc_cfg;      // bulk workgroups per channel were configured: no per-call choice
   int line_per_cu[3];  // resident line workgroups per CU: multi, one, half kernels
   int nslots;
+  int nslots_cfg;   // configured bulk FIFO depth (nslots may be deeper for long stages)
   int device;
   size_t chunk_bytes;
   size_t slot_bytes;
@@ -171,6 +172,7 @@ struct ringsim_comm {
   uint64_t calls;
   int last_proto;
   int last_wpc;
+  int last_group;          // bulk all-reduce: slot steps per stage group of the latest ring call, 0 = whole stages
   int last_tree_channels;  // channels per tree of the latest all-reduce, 0 = ring
   int algo;                // configured all-reduce algorithm
   int last_algo;
@@ -354,6 +356,25 @@ RingArgs call_shape(const ringsim_comm* c, size_t count, int esize) {
 // 8 and 16 ranks from 4 KiB to 512 KiB per rank; from 1-2 MiB up staging
 // wins, by 6-22 us at 4-8 MiB).
 constexpr int64_t kBulkStageMinBytes = 512 * 1024;
+
+// A stage longer than half the configured FIFO depth (in one workgroup's
+// slot steps) made the communicator deepen its FIFOs at init, so that a
+// whole stage fits half of them ("NCCL" book, enqueue chapter:
+// ALLREDUCE_CHUNKSTEPS = NCCL_STEPS / 2). An all-reduce call with such
+// stages instead walks each loop in groups of half the configured depth
+// (every stage moves one group before the next stage runs, as the line
+// protocols do) over the first slots of each FIFO only, so that its FIFO
+// footprint stays at the configured depth: at 16 ranks x 16 channels with
+// 512 KiB chunks the deepened FIFOs take 256 MiB, more than the Infinity
+// Cache holds beside the streaming buffers, and in groups of 4 steps over 8
+// slots 128 MiB (16 ranks x 128 and 256 MiB per rank: 1807 -> 1716 us and
+// 3607 -> 3410 us). Groups change the order of steps, not the fold order of
+// any element.
+int bulk_group_steps(const ringsim_comm* c, const RingArgs& a, int mode, int esize) {
+  const int g = std::max(1, c->nslots_cfg / 2);
+  if (mode != kAllReduce || a.echo || a.nslots <= 2 * g) return 0;
+  return div_up(max_unit_bytes(a, mode, esize), (int64_t)a.slot_bytes) > g ? g : 0;
+}
 
 // Bulk workgroups per channel of one call: a configured count as it is, else
 // fewer than the communicator holds when the stages are short
@@ -596,6 +617,7 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   if ((res = check_device(c)) != RINGSIM_SUCCESS) return res;
   hipStream_t s = static_cast<hipStream_t>(stream);
   c->calls++;
+  c->last_group = 0;
   if (n == 1) {
     // A single rank is a local copy ("NCCL" book, enqueue chapter, taskAppend).
     return launch_local_copy(c, sb, rb, count * esize, s);
@@ -624,6 +646,9 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   if (proto == RINGSIM_PROTO_BULK) {
     const int64_t rank_bytes = (int64_t)(mode == kAllReduce ? count : count * (size_t)n) * esize;
     if (rank_bytes <= kBulkStageMinBytes) a.lds_stage = 0;
+    a.group = bulk_group_steps(c, a, mode, esize);
+    if (a.group > 0) a.nslots = 2 * a.group;
+    c->last_group = a.group;
     c->last_wpc = a.wpc;
     e = launch_ring_bulk(a, mode, dtype, op, s);
   } else {
@@ -863,6 +888,7 @@ ringsim_result_t ringsim_comm_init_config(ringsim_comm_t* comm, int nranks, int 
   c->pipe_mul = std::max(wpc, line_wpc_max);
   for (int k = 0; k < 3; ++k) c->line_per_cu[k] = line_per_cu[k];
   c->nslots = nslots;
+  c->nslots_cfg = cfg.nslots;
   c->device = dev;
   c->chunk_bytes = cfg.chunk_bytes;
   c->slot_bytes = cfg.slot_bytes;
@@ -990,6 +1016,7 @@ ringsim_result_t ringsim_comm_query(ringsim_comm_t comm, ringsim_comm_info_t* in
   info->last_algo = comm->last_algo;
   info->line_max_workgroups_per_channel = comm->line_wpc_max;
   info->last_workgroups_per_channel = comm->last_wpc;
+  info->last_group_steps = comm->last_group;
   info->last_tree_channels = comm->last_tree_channels;
   info->line_fifo_resets = comm->line_resets;
   info->tree_fifo_resets = comm->tree_resets;

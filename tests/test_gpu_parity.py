@@ -493,3 +493,49 @@ def test_bulk_workgroup_counts_switch_on_one_comm():
             _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"bulk switch {coll} count={count} wpc={w}")
     finally:
         rs.comm_destroy(comm)
+
+
+@pytest.mark.parametrize("n,nch,wpc,chunk,dtype", [(4, 1, 1, 524_288, "float32"), (8, 2, 2, 1 << 20, "int64"),
+                                                   (3, 1, 1, 524_288, "bfloat16")])
+def test_bulk_long_stages_in_groups(n, nch, wpc, chunk, dtype):
+    """A stage longer than half the configured FIFO depth (one workgroup per
+    channel moving a whole 512 KiB or 1 MiB chunk: 16 or 32 slot steps)
+    makes the communicator deepen its FIFOs; all-reduce calls with such
+    stages run in groups of 4 steps over the first 8 slots instead, and
+    reduce-scatter, all-gather and short calls on the same communicator use
+    the deepened FIFOs. Several loops and a ragged tail, every result
+    against the oracle."""
+    comm = rs.comm_init(n, nch, "bulk", chunk_bytes=chunk, workgroups_per_channel=wpc)
+    try:
+        info = rs.comm_query(comm)
+        assert info["nslots"] > 8, info
+        e = {"float32": 4, "bfloat16": 2, "int64": 8}[dtype]
+        per_channel = 2 * n * chunk + chunk // 2 + 48
+        big = (nch * per_channel) // e + 3
+        cases = [("allreduce", big, 4), ("reduce_scatter", (2 * chunk + 4096) // e + 1, 0),
+                 ("allreduce", 1000, 0), ("all_gather", (chunk + 4096) // e + 5, 0), ("allreduce", big - 7, 4)]
+        for k, (coll, count, want_group) in enumerate(cases):
+            m = count * n if coll == "reduce_scatter" else count
+            xs = _inputs(n, m, dtype, 2300 + k)
+            send = [G.to_device(x, dtype) for x in xs]
+            out = {"allreduce": m, "reduce_scatter": count, "all_gather": count * n}[coll]
+            recv = [G.empty_like_rank(out, dtype) for _ in range(n)]
+            G.say(f"long stages N={n} C={nch} wpc={wpc} chunk={chunk} {dtype} call {k}: {coll} count={count}")
+            if coll == "allreduce":
+                rs.allreduce(comm, send, recv)
+            elif coll == "reduce_scatter":
+                rs.reduce_scatter(comm, send, recv)
+            else:
+                rs.all_gather(comm, send, recv)
+            G.sync()
+            G.check_comm_ok(comm)
+            assert rs.comm_query(comm)["last_group_steps"] == want_group, (coll, count)
+            if coll == "allreduce":
+                want = oracle.ring_allreduce(xs, "sum", dtype, nchannels=nch, chunk_bytes=chunk)
+            elif coll == "reduce_scatter":
+                want = oracle.ring_reduce_scatter(xs, "sum", dtype, nchannels=nch, chunk_bytes=chunk)
+            else:
+                want = oracle.ring_all_gather(xs, dtype, nchannels=nch, chunk_bytes=chunk)
+            _assert_same([G.to_host(t, dtype) for t in recv], want, dtype, f"{coll} count={count}")
+    finally:
+        rs.comm_destroy(comm)
