@@ -357,23 +357,34 @@ RingArgs call_shape(const ringsim_comm* c, size_t count, int esize) {
 // wins, by 6-22 us at 4-8 MiB).
 constexpr int64_t kBulkStageMinBytes = 512 * 1024;
 
-// A stage longer than half the configured FIFO depth (in one workgroup's
-// slot steps) made the communicator deepen its FIFOs at init, so that a
-// whole stage fits half of them ("NCCL" book, enqueue chapter:
-// ALLREDUCE_CHUNKSTEPS = NCCL_STEPS / 2). An all-reduce call with such
-// stages instead walks each loop in groups of half the configured depth
-// (every stage moves one group before the next stage runs, as the line
-// protocols do) over the first slots of each FIFO only, so that its FIFO
-// footprint stays at the configured depth: at 16 ranks x 16 channels with
-// 512 KiB chunks the deepened FIFOs take 256 MiB, more than the Infinity
-// Cache holds beside the streaming buffers, and in groups of 4 steps over 8
-// slots 128 MiB (16 ranks x 128 and 256 MiB per rank: 1807 -> 1716 us and
-// 3607 -> 3410 us). Groups change the order of steps, not the fold order of
-// any element.
-int bulk_group_steps(const ringsim_comm* c, const RingArgs& a, int mode, int esize) {
-  const int g = std::max(1, c->nslots_cfg / 2);
-  if (mode != kAllReduce || a.echo || a.nslots <= 2 * g) return 0;
-  return div_up(max_unit_bytes(a, mode, esize), (int64_t)a.slot_bytes) > g ? g : 0;
+// FIFO depth and step groups of one bulk call. A stage longer than half the
+// configured depth (in one workgroup's slot steps) made the communicator
+// deepen its FIFOs at init, so that a whole stage fits half of them ("NCCL"
+// book, enqueue chapter: ALLREDUCE_CHUNKSTEPS = NCCL_STEPS / 2). A call
+// keeps its FIFO footprint at the configured depth wherever it can: one
+// whose stages fit half the configured depth uses only that many slots of
+// each FIFO, and an all-reduce with longer stages walks each loop in groups
+// of half the configured depth (every stage moves one group before the next
+// stage runs, as the line protocols do) over those slots. At 16 ranks x 16
+// channels with 512 KiB chunks the deepened FIFOs take 256 MiB, more than
+// the Infinity Cache holds beside the streaming buffers; in groups of 4
+// steps over 8 slots 128 MiB (16 ranks x 128 and 256 MiB per rank: 1807 ->
+// 1726 us and 3607 -> 3417 us). Only reduce-scatter and all-gather calls
+// with long stages use the deepened FIFOs (the grouped kernel is built for
+// the all-reduce), and the debug FIFO records keep the full depth. Groups
+// change the order of steps, not the fold order of any element. Returns the
+// group length (0 = whole stages) and sets a->nslots.
+int bulk_call_depth(const ringsim_comm* c, RingArgs* a, int mode, int esize) {
+  const int cfg = std::max(2, std::min(c->nslots_cfg, c->nslots));
+  if (a->echo || a->nslots <= cfg) return 0;
+  const int64_t steps = div_up(max_unit_bytes(*a, mode, esize), (int64_t)a->slot_bytes);
+  if (2 * steps <= cfg) {
+    a->nslots = cfg;
+    return 0;
+  }
+  if (mode != kAllReduce) return 0;
+  a->nslots = 2 * (cfg / 2);
+  return cfg / 2;
 }
 
 // Bulk workgroups per channel of one call: a configured count as it is, else
@@ -646,8 +657,7 @@ ringsim_result_t run_ring(ringsim_comm* c, int mode, const void* const* sb, void
   if (proto == RINGSIM_PROTO_BULK) {
     const int64_t rank_bytes = (int64_t)(mode == kAllReduce ? count : count * (size_t)n) * esize;
     if (rank_bytes <= kBulkStageMinBytes) a.lds_stage = 0;
-    a.group = bulk_group_steps(c, a, mode, esize);
-    if (a.group > 0) a.nslots = 2 * a.group;
+    a.group = bulk_call_depth(c, &a, mode, esize);
     c->last_group = a.group;
     c->last_wpc = a.wpc;
     e = launch_ring_bulk(a, mode, dtype, op, s);
